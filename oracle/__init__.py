@@ -1,0 +1,224 @@
+"""CPU oracle for the MXNorm forward path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps the plain C reference in ``mx_oracle.c`` with
+numpy arrays; it shares no code with the GPU library and never calls it.
+
+Array conventions: bf16 data travels as ``numpy.uint16`` bit patterns,
+row-major ``[rows, hidden]``; codes and scales are ``numpy.uint8``.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+E4M3 = 0
+E2M1 = 1
+BLOCK = 32
+
+_lib = None
+
+
+def lib():
+    """Load the compiled oracle, compiling it first only if it is missing."""
+    global _lib
+    if _lib is None:
+        # MXO_LIB lets the mutation tests load a deliberately broken build.
+        path = os.environ.get("MXO_LIB", _build.LIB)
+        if not os.path.exists(path):
+            _build.build()
+        L = C.CDLL(path)
+        u16p = C.POINTER(C.c_uint16)
+        u8p = C.POINTER(C.c_uint8)
+        f32p = C.POINTER(C.c_float)
+        i64 = C.c_int64
+        L.mxo_bf16_decode.restype = C.c_double
+        L.mxo_bf16_decode.argtypes = [C.c_uint16]
+        L.mxo_bf16_encode_rne.restype = C.c_uint16
+        L.mxo_bf16_encode_rne.argtypes = [C.c_float]
+        L.mxo_e4m3_decode.restype = C.c_double
+        L.mxo_e4m3_decode.argtypes = [C.c_uint8]
+        L.mxo_e2m1_decode.restype = C.c_double
+        L.mxo_e2m1_decode.argtypes = [C.c_uint8]
+        L.mxo_e4m3_encode.restype = C.c_uint8
+        L.mxo_e4m3_encode.argtypes = [C.c_double]
+        L.mxo_e2m1_encode.restype = C.c_uint8
+        L.mxo_e2m1_encode.argtypes = [C.c_double]
+        L.mxo_scale_exponent.restype = C.c_int
+        L.mxo_scale_exponent.argtypes = [C.c_double, C.c_int]
+        L.mxo_mx_quant.restype = C.c_int
+        L.mxo_mx_quant.argtypes = [u16p, i64, i64, C.c_int, u8p, u8p]
+        L.mxo_mxnorm_fwd.restype = C.c_int
+        L.mxo_mxnorm_fwd.argtypes = [u16p, u16p, i64, i64, C.c_int, C.c_float, C.c_int,
+                                     u8p, u8p, f32p]
+        L.mxo_mxnorm_hadamard_fwd.restype = C.c_int
+        L.mxo_mxnorm_hadamard_fwd.argtypes = [u16p, u16p, i64, i64, C.c_int, C.c_float,
+                                              C.c_int, C.c_int, u8p, u8p, f32p]
+        L.mxo_rmsnorm_mxquant_fwd.restype = C.c_int
+        L.mxo_rmsnorm_mxquant_fwd.argtypes = [u16p, u16p, i64, i64, C.c_float, C.c_int,
+                                              u16p, u8p, u8p, f32p]
+        L.mxo_row_stat.restype = C.c_int
+        L.mxo_row_stat.argtypes = [u16p, i64, C.c_int, C.c_int, C.POINTER(C.c_int),
+                                   C.POINTER(C.c_uint64)]
+        L.mxo_rho.restype = C.c_float
+        L.mxo_rho.argtypes = [C.c_int, C.c_uint64, i64, C.c_int, C.c_float]
+        L.mxo_fwht_f32.restype = None
+        L.mxo_fwht_f32.argtypes = [f32p, i64, C.c_int]
+        L.mxo_bf16_encode_array.restype = None
+        L.mxo_bf16_encode_array.argtypes = [f32p, i64, u16p]
+        L.mxo_encode_array.restype = None
+        L.mxo_encode_array.argtypes = [C.POINTER(C.c_double), i64, C.c_int, u8p]
+        L.mxo_max_threads.restype = C.c_int
+        L.mxo_max_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def _bf16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 data must be passed as uint16 bit patterns")
+    return a
+
+
+def emax(elem):
+    return 8 if elem == E4M3 else 2
+
+
+def codes_cols(hidden, elem):
+    return hidden if elem == E4M3 else hidden // 2
+
+
+def _check(status, name):
+    if status != 0:
+        raise ValueError("%s: invalid arguments (status %d)" % (name, status))
+
+
+# ---- scalar / bulk format helpers -------------------------------------------------
+
+def bf16_decode(b):
+    return lib().mxo_bf16_decode(int(b))
+
+
+def bf16_encode_rne(f):
+    return lib().mxo_bf16_encode_rne(float(f))
+
+
+def bf16_encode_array(f32):
+    f32 = np.ascontiguousarray(f32, dtype=np.float32)
+    out = np.empty(f32.shape, dtype=np.uint16)
+    lib().mxo_bf16_encode_array(_ptr(f32, C.c_float), f32.size, _ptr(out, C.c_uint16))
+    return out
+
+
+def e4m3_decode(c):
+    return lib().mxo_e4m3_decode(int(c))
+
+
+def e2m1_decode(c):
+    return lib().mxo_e2m1_decode(int(c))
+
+
+def e4m3_encode(v):
+    return lib().mxo_e4m3_encode(float(v))
+
+
+def e2m1_encode(v):
+    return lib().mxo_e2m1_encode(float(v))
+
+
+def encode_array(v, elem):
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().mxo_encode_array(_ptr(v, C.c_double), v.size, elem, _ptr(out, C.c_uint8))
+    return out
+
+
+def scale_exponent(amax, em):
+    return lib().mxo_scale_exponent(float(amax), int(em))
+
+
+def row_stat(xrow, p, elem):
+    xrow = _bf16(xrow)
+    E = C.c_int()
+    S = C.c_uint64()
+    _check(lib().mxo_row_stat(_ptr(xrow, C.c_uint16), xrow.size, p, emax(elem),
+                              C.byref(E), C.byref(S)), "row_stat")
+    return E.value, S.value
+
+
+def rho(E, S, K, p, c):
+    return lib().mxo_rho(int(E), int(S), int(K), int(p), float(c))
+
+
+def fwht_f32(y, had):
+    y = np.array(y, dtype=np.float32, copy=True)
+    lib().mxo_fwht_f32(_ptr(y, C.c_float), y.size, had)
+    return y
+
+
+# ---- whole-matrix entry points (same names as the GPU library) --------------------
+
+def mx_quant(x, elem):
+    x = _bf16(x)
+    rows, hidden = x.shape
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    _check(lib().mxo_mx_quant(_ptr(x, C.c_uint16), rows, hidden, elem,
+                              _ptr(codes, C.c_uint8), _ptr(scales, C.c_uint8)), "mx_quant")
+    return codes, scales
+
+
+def mxnorm_fwd(x, gamma, p, c, elem):
+    x = _bf16(x)
+    rows, hidden = x.shape
+    g = None if gamma is None else _bf16(gamma)
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    rrms = np.zeros((rows,), dtype=np.float32)
+    _check(lib().mxo_mxnorm_fwd(_ptr(x, C.c_uint16), _ptr(g, C.c_uint16), rows, hidden,
+                                p, c, elem, _ptr(codes, C.c_uint8), _ptr(scales, C.c_uint8),
+                                _ptr(rrms, C.c_float)), "mxnorm_fwd")
+    return codes, scales, rrms
+
+
+def mxnorm_hadamard_fwd(x, gamma, p, c, had, elem):
+    x = _bf16(x)
+    rows, hidden = x.shape
+    g = None if gamma is None else _bf16(gamma)
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    rrms = np.zeros((rows,), dtype=np.float32)
+    _check(lib().mxo_mxnorm_hadamard_fwd(_ptr(x, C.c_uint16), _ptr(g, C.c_uint16), rows,
+                                         hidden, p, c, had, elem, _ptr(codes, C.c_uint8),
+                                         _ptr(scales, C.c_uint8), _ptr(rrms, C.c_float)),
+           "mxnorm_hadamard_fwd")
+    return codes, scales, rrms
+
+
+def rmsnorm_mxquant_fwd(x, gamma, eps, elem):
+    x = _bf16(x)
+    rows, hidden = x.shape
+    g = None if gamma is None else _bf16(gamma)
+    y = np.zeros((rows, hidden), dtype=np.uint16)
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    rstd = np.zeros((rows,), dtype=np.float32)
+    _check(lib().mxo_rmsnorm_mxquant_fwd(_ptr(x, C.c_uint16), _ptr(g, C.c_uint16), rows,
+                                         hidden, eps, elem, _ptr(y, C.c_uint16),
+                                         _ptr(codes, C.c_uint8), _ptr(scales, C.c_uint8),
+                                         _ptr(rstd, C.c_float)), "rmsnorm_mxquant_fwd")
+    return y, codes, scales, rstd
+
+
+def max_threads():
+    return lib().mxo_max_threads()
