@@ -1,0 +1,156 @@
+/*
+ * mxnorm.h -- C ABI of the MI355X (gfx950) MXNorm library, libmxnorm.so.
+ *
+ * MXNorm is a drop-in replacement for RMSNorm that emits the row already cast
+ * to an MX format and estimates the row's inverse RMS from the E8M0 block
+ * scales of that cast.  Sources, cited by page title and section:
+ *   [P1] "MXNorm: Reusing MXFP block scales for efficient tensor
+ *        normalisation", gist.science summary (Spanish), "Resumen tecnico".
+ *   [P2] the same paper, gptget.net summary (Chinese) with the authors'
+ *        English abstract.
+ *   [P3] summary of the MXFP4 pre-training study on AMD MI355X,
+ *        gist.science (Spanish), "Metodologia" and "Hallazgos" 2.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates and frees nothing, keeps no global state, never synchronises
+ *     the stream, and may be called from several host threads at once.
+ *   - Matrices are row-major with contiguous rows (row stride = hidden).
+ *     bf16 data is passed as raw 16-bit patterns.
+ *   - Block size is 32 elements along the hidden dimension; hidden must be a
+ *     multiple of 32 and at most MXQ_MAX_HIDDEN.
+ *   - Outputs of an MX cast (the "MX tensor"):
+ *       codes : E4M3 -> rows*hidden bytes, one OCP E4M3 ("FN") code per
+ *               element; E2M1 -> rows*hidden/2 bytes, two OCP E2M1 codes per
+ *               byte, element 2j in the low nibble of byte j.
+ *       scales: rows*(hidden/32) bytes, E8M0 (value 2^(byte-127)); 0xFF is
+ *               the NaN scale, used for any block holding NaN or Inf.
+ *     Element rule (OCP MX): scale exponent e = floor(log2(block absmax))
+ *     - emax (emax 8 for E4M3, 2 for E2M1), clamped to [-127, 127]; an
+ *     all-zero block takes e = -127.  Each element is value / 2^e rounded to
+ *     the nearest code, ties to the even code, saturating at +-448 (E4M3) or
+ *     +-6 (E2M1); the sign of zero is kept.  Codes under a 0xFF scale are
+ *     unspecified.
+ *   - Alignment: x, codes and any bf16 workspace must be 16-byte aligned;
+ *     gamma 16-byte aligned; scales and rrms/rstd need natural alignment only.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns
+ *     immediately.  A device fault surfaces at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - Errors are reported before anything is launched; rows == 0 is a valid
+ *     no-op.
+ */
+#ifndef MXNORM_H
+#define MXNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque HIP stream handle (hipStream_t); 0 selects the null stream. */
+typedef void *mxq_stream_t;
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_EINVAL = -1,        /* bad shape, NULL pointer, bad p / c / eps / had */
+    MXQ_EALIGN = -2,        /* a pointer is not aligned as required above */
+    MXQ_EUNSUPPORTED = -3,  /* valid arguments outside what this build supports */
+    MXQ_EHIP = -4           /* the HIP runtime refused the launch */
+} mxq_status;
+
+typedef enum {
+    MXQ_E4M3 = 0,           /* MXFP8: E4M3 elements, 1 byte each */
+    MXQ_E2M1 = 1            /* MXFP4: E2M1 elements, 2 per byte */
+} mxq_elem;
+
+#define MXQ_BLOCK 32
+#define MXQ_MAX_HIDDEN 32768
+
+/*
+ * mx_quant -- MXCast of a bf16 matrix [rows, hidden] into an MX tensor.
+ * The stand-alone cast that follows RMSNorm in the unfused pipeline
+ * ([P1] §1; [P2] abstract: block scales computed by the MXFP8 cast).
+ *   x      : device bf16 [rows, hidden]
+ *   codes  : device out, layout above
+ *   scales : device out, [rows, hidden/32]
+ */
+mxq_status mx_quant(const void *x, int64_t rows, int64_t hidden, mxq_elem elem,
+                    uint8_t *codes, uint8_t *scales, mxq_stream_t stream);
+
+/*
+ * mxnorm_fwd -- MXNorm forward, one pass over x ([P1] §2 "Implementacion":
+ * block absmax, RMS estimate, scaling and quantisation scales fused; [P1] §2
+ * "Formula" for the estimate; [P1] §3 for the 32x smaller reduction).
+ *   Per row: mt_k = 2^(e_k + emax) with e_k the E8M0 exponent the MX cast of
+ *   x gives block k; E = max_k (e_k + emax);
+ *   S = sum_k 2^(40 - p (E - e_k - emax)) over the terms with exponent >= 0
+ *   (an exact integer); rho = fl(c / r) * 2^(40/p - E) with
+ *   r = fl(fl(S)/K) (p = 1) or fl(sqrt(fl(fl(S)/K))) (p = 2), all fp32
+ *   correctly rounded; this is c * ((1/K) sum mt_k^p)^(-1/p).
+ *   y_i = fl(x_i * rho), then fl(y_i * gamma_i) if gamma is given; y is then
+ *   MX-cast with scales taken from y.  A row holding NaN/Inf gets rho = NaN
+ *   and all-0xFF scales.
+ *   gamma  : device bf16 [hidden], or NULL (the MXNormLinear mode of [P1] §2,
+ *            where the gain is folded into the next linear layer)
+ *   p      : 1 (arithmetic mean) or 2 (quadratic mean)
+ *   c      : correction constant c(p, 32) > 0; 0 selects mxnorm_default_c(p)
+ *   rrms   : device fp32 [rows] receiving rho (the inverse-RMS estimate kept
+ *            for the straight-through backward of [P1] §2), or NULL
+ */
+mxq_status mxnorm_fwd(const void *x, const void *gamma, int64_t rows, int64_t hidden,
+                      int p, float c, mxq_elem elem, uint8_t *codes, uint8_t *scales,
+                      float *rrms, mxq_stream_t stream);
+
+/*
+ * mxnorm_hadamard_fwd -- mxnorm_fwd followed, before the cast, by a fixed
+ * normalised Sylvester Hadamard rotation of every group of `had` consecutive
+ * elements ([P3] "Metodologia" and "Hallazgos" 2: deterministic H16 / H32
+ * rotation before MXFP4 quantisation).  rho is the same as mxnorm_fwd's
+ * (taken from the unrotated input).  The rotation is a fast Walsh-Hadamard
+ * transform in fp32 with butterfly distances 1, 2, 4, ... (each butterfly
+ * (a, b) -> (a + b, a - b)), then multiplied by fl(1/sqrt(had)) (0.25 for 16).
+ *   had    : 16 or 32
+ *   other arguments as mxnorm_fwd
+ */
+mxq_status mxnorm_hadamard_fwd(const void *x, const void *gamma, int64_t rows,
+                               int64_t hidden, int p, float c, int had, mxq_elem elem,
+                               uint8_t *codes, uint8_t *scales, float *rrms,
+                               mxq_stream_t stream);
+
+/*
+ * rmsnorm_mxquant_fwd -- the two-pass pipeline MXNorm replaces ([P1] §1:
+ * RMSNorm and the MX cast as separate operations; [P1] §3: the
+ * high-precision intermediate makes a round trip through memory).
+ *   pass 1: rstd = 1/sqrt(mean(x^2) + eps) (fp32 accumulation),
+ *           y = bf16(fl(fl(x * rstd) * gamma)) written to y_workspace;
+ *   pass 2: mx_quant(y_workspace).
+ *   y_workspace : device bf16 [rows, hidden], caller-owned scratch that
+ *                 holds y on return
+ *   rstd        : device fp32 [rows], or NULL
+ *   eps         : >= 0, finite
+ */
+mxq_status rmsnorm_mxquant_fwd(const void *x, const void *gamma, int64_t rows,
+                               int64_t hidden, float eps, mxq_elem elem,
+                               void *y_workspace, uint8_t *codes, uint8_t *scales,
+                               float *rstd, mxq_stream_t stream);
+
+/*
+ * mxnorm_default_c -- host function.  Default c(p, 32) for power-of-two block
+ * magnitudes and Gaussian activations with a log-uniform row scale (the
+ * pages call the constant precalculated but print no value; [P1] §2
+ * "Fundamentos Teoricos").  Returns 0 for p outside {1, 2}.
+ */
+float mxnorm_default_c(int p);
+
+/* mxq_status_str -- host function: a static, human-readable status name. */
+const char *mxq_status_str(mxq_status s);
+
+/* mxq_version -- host function: library version string. */
+const char *mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXNORM_H */

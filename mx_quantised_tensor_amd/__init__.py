@@ -1,0 +1,178 @@
+"""MXNorm for AMD MI355X (gfx950): Python binding of libmxnorm.so.
+
+Thin ctypes marshalling over the C ABI in ``include/mxnorm.h``: every step
+of the computation runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current HIP stream; tensors in and out are
+``torch.bfloat16`` (or int16/uint16 bit patterns) for bf16 data,
+``torch.uint8`` for codes and scales, ``torch.float32`` for rrms / rstd.
+
+The library is loaded from ``mx_quantised_tensor_amd/lib/libmxnorm.so``;
+if it is missing, importing a kernel entry point raises -- there is no
+fallback path.
+"""
+import ctypes as C
+import os
+
+import torch
+
+__all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
+           "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
+           "library_path"]
+
+E4M3 = 0
+E2M1 = 1
+BLOCK = 32
+MAX_HIDDEN = 32768
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libmxnorm.so")
+_lib = None
+
+EXPORTED = ("mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd",
+            "mxnorm_default_c", "mxq_status_str", "mxq_version")
+
+
+class MxqError(RuntimeError):
+    pass
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmxnorm.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MxqError("libmxnorm.so not built: run __graft_entry__.build() or "
+                           "python mx_quantised_tensor_amd/build.py (looked for %s)" % _LIB_PATH)
+        L = C.CDLL(_LIB_PATH)
+        vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
+        L.mx_quant.restype = i32
+        L.mx_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.mxnorm_fwd.restype = i32
+        L.mxnorm_fwd.argtypes = [vp, vp, i64, i64, i32, f32, i32, vp, vp, vp, vp]
+        L.mxnorm_hadamard_fwd.restype = i32
+        L.mxnorm_hadamard_fwd.argtypes = [vp, vp, i64, i64, i32, f32, i32, i32, vp, vp, vp, vp]
+        L.rmsnorm_mxquant_fwd.restype = i32
+        L.rmsnorm_mxquant_fwd.argtypes = [vp, vp, i64, i64, f32, i32, vp, vp, vp, vp, vp]
+        L.mxnorm_default_c.restype = f32
+        L.mxnorm_default_c.argtypes = [i32]
+        L.mxq_status_str.restype = C.c_char_p
+        L.mxq_status_str.argtypes = [i32]
+        L.mxq_version.restype = C.c_char_p
+        L.mxq_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().mxq_status_str(status).decode()
+
+
+def mxnorm_default_c(p: int) -> float:
+    return float(lib().mxnorm_default_c(int(p)))
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        raise MxqError("%s failed: %s" % (name, status_str(status)))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _bf16_2d(x):
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D [rows, hidden] tensor")
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("bf16 data must be torch.bfloat16 (or 16-bit integer bit patterns)")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    return x
+
+
+def _gamma(g, hidden):
+    if g is None:
+        return None
+    if g.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or g.numel() != hidden:
+        raise ValueError("gamma must be bf16 with `hidden` elements")
+    if not g.is_cuda or not g.is_contiguous():
+        raise ValueError("gamma must be a contiguous device tensor")
+    return g
+
+
+def _outputs(x, elem, codes, scales):
+    rows, hidden = x.shape
+    ccols = hidden if elem == E4M3 else hidden // 2
+    if codes is None:
+        codes = torch.empty((rows, ccols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, hidden // BLOCK), dtype=torch.uint8, device=x.device)
+    if codes.numel() != rows * ccols or scales.numel() != rows * (hidden // BLOCK):
+        raise ValueError("codes / scales have the wrong size")
+    return codes, scales
+
+
+def mx_quant(x, elem=E4M3, codes=None, scales=None, stream=None):
+    """MX cast of bf16 x [rows, hidden] -> (codes, scales)."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    codes, scales = _outputs(x, elem, codes, scales)
+    _check(lib().mx_quant(_ptr(x), rows, hidden, elem, _ptr(codes), _ptr(scales),
+                          _stream(stream)), "mx_quant")
+    return codes, scales
+
+
+def mxnorm_fwd(x, gamma=None, p=2, c=0.0, elem=E4M3, codes=None, scales=None, rrms=None,
+               want_rrms=True, stream=None):
+    """MXNorm forward -> (codes, scales, rrms).  c = 0 selects the default c(p)."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    gamma = _gamma(gamma, hidden)
+    codes, scales = _outputs(x, elem, codes, scales)
+    if rrms is None and want_rrms:
+        rrms = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(lib().mxnorm_fwd(_ptr(x), _ptr(gamma), rows, hidden, p, c, elem, _ptr(codes),
+                            _ptr(scales), _ptr(rrms), _stream(stream)), "mxnorm_fwd")
+    return codes, scales, rrms
+
+
+def mxnorm_hadamard_fwd(x, gamma=None, p=2, c=0.0, had=16, elem=E2M1, codes=None, scales=None,
+                        rrms=None, want_rrms=True, stream=None):
+    """MXNorm forward with an H16/H32 rotation before the cast."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    gamma = _gamma(gamma, hidden)
+    codes, scales = _outputs(x, elem, codes, scales)
+    if rrms is None and want_rrms:
+        rrms = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(lib().mxnorm_hadamard_fwd(_ptr(x), _ptr(gamma), rows, hidden, p, c, had, elem,
+                                     _ptr(codes), _ptr(scales), _ptr(rrms), _stream(stream)),
+           "mxnorm_hadamard_fwd")
+    return codes, scales, rrms
+
+
+def rmsnorm_mxquant_fwd(x, gamma=None, eps=1e-5, elem=E4M3, y=None, codes=None, scales=None,
+                        rstd=None, want_rstd=True, stream=None):
+    """Two-pass baseline: RMSNorm to bf16 y, then mx_quant(y) -> (y, codes, scales, rstd)."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    gamma = _gamma(gamma, hidden)
+    codes, scales = _outputs(x, elem, codes, scales)
+    if y is None:
+        y = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device)
+    if rstd is None and want_rstd:
+        rstd = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(lib().rmsnorm_mxquant_fwd(_ptr(x), _ptr(gamma), rows, hidden, eps, elem, _ptr(y),
+                                     _ptr(codes), _ptr(scales), _ptr(rstd), _stream(stream)),
+           "rmsnorm_mxquant_fwd")
+    return y, codes, scales, rstd

@@ -1,0 +1,140 @@
+// mxnorm_capi.cpp -- the C ABI of libmxnorm.so (declared in include/mxnorm.h):
+// argument validation, defaults and kernel dispatch.  Every check runs on the
+// host before anything is enqueued; the library never allocates, frees or
+// synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "mxnorm.h"
+
+namespace {
+
+// Default c(p, 32): Gaussian activations, log-uniform row scale, power-of-two
+// block magnitudes: c = (E[M^p] (1 - 2^-p) / (p ln 2))^(1/p) with M the max of
+// 32 i.i.d. |N(0,1)| (E[M] = 2.3470792, E[M^2] = 5.7095053), rounded to fp32.
+constexpr float kDefaultC1 = 0x1.b16c5ep+0f;  // 1.6930598
+constexpr float kDefaultC2 = 0x1.c1ed54p+0f;  // 1.7575276
+
+// Largest element count per call: keeps every grid dimension below 2^32.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+mxq_status check_shape(int64_t rows, int64_t hidden, mxq_elem elem) {
+  if (rows < 0 || hidden <= 0 || hidden % MXQ_BLOCK != 0) return MXQ_EINVAL;
+  if (elem != MXQ_E4M3 && elem != MXQ_E2M1) return MXQ_EINVAL;
+  if (hidden > MXQ_MAX_HIDDEN || !mxq::row_shape_supported((int)hidden))
+    return MXQ_EUNSUPPORTED;
+  if (rows > kMaxElems / hidden) return MXQ_EUNSUPPORTED;
+  return MXQ_OK;
+}
+
+mxq_status check_mx_outputs(const void* x, const uint8_t* codes, const uint8_t* scales) {
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return MXQ_EALIGN;
+  return MXQ_OK;
+}
+
+mxq_status status_of(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
+
+mxq_status mxnorm_common(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
+                         float c, int had, mxq_elem elem, uint8_t* codes, uint8_t* scales,
+                         float* rrms, mxq_stream_t stream) {
+  mxq_status st = check_shape(rows, hidden, elem);
+  if (st != MXQ_OK) return st;
+  if (p != 1 && p != 2) return MXQ_EINVAL;
+  if (!(c >= 0.0f) || !isfinite(c)) return MXQ_EINVAL;
+  if (had != 0 && had != 16 && had != 32) return MXQ_EINVAL;
+  if (rows == 0) return MXQ_OK;
+  st = check_mx_outputs(x, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_EALIGN;
+  if (rrms != nullptr && !aligned(rrms, 4)) return MXQ_EALIGN;
+  mxq::MxnormArgs a;
+  a.x = x;
+  a.gamma = gamma;
+  a.rows = rows;
+  a.hidden = (int)hidden;
+  a.p = p;
+  a.c = c == 0.0f ? mxnorm_default_c(p) : c;
+  a.had = had;
+  a.elem = (int)elem;
+  a.codes = codes;
+  a.scales = scales;
+  a.rrms = rrms;
+  a.stream = stream;
+  (void)hipGetLastError();  // clear an unrelated earlier error
+  return status_of(mxq::launch_mxnorm(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+mxq_status mx_quant(const void* x, int64_t rows, int64_t hidden, mxq_elem elem, uint8_t* codes,
+                    uint8_t* scales, mxq_stream_t stream) {
+  mxq_status st = check_shape(rows, hidden, elem);
+  if (st != MXQ_OK) return st;
+  if (rows == 0) return MXQ_OK;
+  st = check_mx_outputs(x, codes, scales);
+  if (st != MXQ_OK) return st;
+  (void)hipGetLastError();
+  return status_of(mxq::launch_mx_quant(x, rows, (int)hidden, (int)elem, codes, scales, stream));
+}
+
+mxq_status mxnorm_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
+                      float c, mxq_elem elem, uint8_t* codes, uint8_t* scales, float* rrms,
+                      mxq_stream_t stream) {
+  return mxnorm_common(x, gamma, rows, hidden, p, c, 0, elem, codes, scales, rrms, stream);
+}
+
+mxq_status mxnorm_hadamard_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden,
+                               int p, float c, int had, mxq_elem elem, uint8_t* codes,
+                               uint8_t* scales, float* rrms, mxq_stream_t stream) {
+  if (had != 16 && had != 32) return MXQ_EINVAL;
+  return mxnorm_common(x, gamma, rows, hidden, p, c, had, elem, codes, scales, rrms, stream);
+}
+
+mxq_status rmsnorm_mxquant_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden,
+                               float eps, mxq_elem elem, void* y_workspace, uint8_t* codes,
+                               uint8_t* scales, float* rstd, mxq_stream_t stream) {
+  mxq_status st = check_shape(rows, hidden, elem);
+  if (st != MXQ_OK) return st;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MXQ_EINVAL;
+  if (rows == 0) return MXQ_OK;
+  st = check_mx_outputs(x, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (y_workspace == nullptr) return MXQ_EINVAL;
+  if (!aligned(y_workspace, 16)) return MXQ_EALIGN;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_EALIGN;
+  if (rstd != nullptr && !aligned(rstd, 4)) return MXQ_EALIGN;
+  (void)hipGetLastError();
+  hipError_t e = mxq::launch_rmsnorm(x, gamma, rows, (int)hidden, eps, y_workspace, rstd, stream);
+  if (e != hipSuccess) return MXQ_EHIP;
+  return status_of(
+      mxq::launch_mx_quant(y_workspace, rows, (int)hidden, (int)elem, codes, scales, stream));
+}
+
+float mxnorm_default_c(int p) {
+  if (p == 1) return kDefaultC1;
+  if (p == 2) return kDefaultC2;
+  return 0.0f;
+}
+
+const char* mxq_status_str(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_EINVAL: return "MXQ_EINVAL: invalid argument";
+    case MXQ_EALIGN: return "MXQ_EALIGN: pointer misaligned";
+    case MXQ_EUNSUPPORTED: return "MXQ_EUNSUPPORTED: shape outside this build's limits";
+    case MXQ_EHIP: return "MXQ_EHIP: HIP launch failed";
+  }
+  return "MXQ_UNKNOWN";
+}
+
+const char* mxq_version(void) { return "mxnorm-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+"""Comparison rules between the GPU library and the CPU oracle (tests only).
+
+  * E8M0 scales: byte-equal.
+  * rho (rrms): bit-equal, NaN where the oracle has NaN.
+  * element codes: the step distance is the difference of ranks in the ordered
+    list of representable values (-max ... -0, +0 ... +max); codes under a
+    0xFF (NaN) scale are not compared.  The acceptance bar is at most one
+    step on at most 0.01% of the elements; the MXNorm kernels are designed to
+    reach zero and the tests say which bar they hold.
+"""
+import numpy as np
+import torch
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def from_device(t):
+    return t.detach().cpu().numpy()
+
+
+def code_ranks(codes: np.ndarray, elem: int) -> np.ndarray:
+    """Signed rank of every element code (E2M1 bytes are unpacked)."""
+    if elem == 0:
+        m = (codes & 0x7F).astype(np.int64)
+        neg = (codes & 0x80) != 0
+    else:
+        lo, hi = codes & 0x0F, codes >> 4
+        c = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+        c[..., 0::2] = lo
+        c[..., 1::2] = hi
+        m = (c & 0x7).astype(np.int64)
+        neg = (c & 0x8) != 0
+    return np.where(neg, -m - 1, m)
+
+
+def code_step_stats(got, want, scales_want, elem):
+    """(max step, fraction of elements with a nonzero step, count) over the
+    elements whose block scale is not NaN."""
+    rg, rw = code_ranks(got, elem), code_ranks(want, elem)
+    valid = np.repeat(scales_want != 0xFF, 32, axis=-1)
+    d = np.abs(rg - rw)[valid]
+    if d.size == 0:
+        return 0, 0.0, 0
+    return int(d.max()), float(np.count_nonzero(d)) / d.size, int(np.count_nonzero(d))
+
+
+def assert_codes(got, want, scales_want, elem, exact=True, what=""):
+    mx, frac, n = code_step_stats(got, want, scales_want, elem)
+    if exact:
+        assert n == 0, "%s: %d element codes differ (max step %d)" % (what, n, mx)
+    else:
+        assert mx <= 1 and frac <= 1e-4, "%s: max step %d on %.3g of elements" % (what, mx, frac)
+
+
+def assert_scales_equal(got, want, what=""):
+    bad = np.count_nonzero(got != want)
+    assert bad == 0, "%s: %d of %d scales differ" % (what, bad, want.size)
+
+
+def assert_rho_equal(got, want, what=""):
+    gb = got.view(np.uint32)
+    wb = want.view(np.uint32)
+    nan_w = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan_w), what + ": NaN pattern differs"
+    bad = np.count_nonzero(gb[~nan_w] != wb[~nan_w])
+    assert bad == 0, "%s: %d of %d rho values differ (max rel %.3g)" % (
+        what, bad, want.size,
+        np.max(np.abs(got[~nan_w].astype(np.float64) / want[~nan_w] - 1)) if bad else 0)

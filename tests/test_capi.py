@@ -1,0 +1,143 @@
+"""C ABI of libmxnorm.so on the host (no GPU): the library loads, exports every
+function include/mxnorm.h declares, and rejects bad arguments before it
+touches the GPU.  Only argument checks run here; no kernel is launched."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mx_quantised_tensor_amd as mxq
+from oracle import derive_c
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxnorm.h")
+
+OK, EINVAL, EALIGN, EUNSUP = 0, -1, -2, -3
+A16 = 0x10000    # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10008    # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mxq.lib()
+    names = declared_functions()
+    assert set(names) >= {"mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd",
+                          "rmsnorm_mxquant_fwd", "mxnorm_default_c", "mxq_status_str"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert mxq.lib().mxq_version().decode().startswith("mxnorm-gfx950")
+
+
+def test_default_c_matches_derivation():
+    for p in (1, 2):
+        want = np.float32(derive_c.c_pow2_scale(p))
+        assert np.float32(mxq.mxnorm_default_c(p)) == want
+    assert mxq.mxnorm_default_c(3) == 0.0
+
+
+def test_status_strings():
+    for s in (OK, EINVAL, EALIGN, EUNSUP, -4):
+        assert mxq.status_str(s).startswith("MXQ_")
+
+
+def _mxq(x=A16, rows=4, hidden=64, elem=0, codes=A16, scales=A16):
+    return mxq.lib().mx_quant(x, rows, hidden, elem, codes, scales, None)
+
+
+def _mxn(x=A16, g=None, rows=4, hidden=64, p=2, c=0.0, elem=0, codes=A16, scales=A16, rrms=None):
+    return mxq.lib().mxnorm_fwd(x, g, rows, hidden, p, c, elem, codes, scales, rrms, None)
+
+
+def _had(had=16, **kw):
+    a = dict(x=A16, g=None, rows=4, hidden=64, p=2, c=0.0, elem=1, codes=A16, scales=A16,
+             rrms=None)
+    a.update(kw)
+    return mxq.lib().mxnorm_hadamard_fwd(a["x"], a["g"], a["rows"], a["hidden"], a["p"], a["c"],
+                                         had, a["elem"], a["codes"], a["scales"], a["rrms"], None)
+
+
+def _rms(x=A16, g=None, rows=4, hidden=64, eps=1e-5, elem=0, y=A16, codes=A16, scales=A16,
+         rstd=None):
+    return mxq.lib().rmsnorm_mxquant_fwd(x, g, rows, hidden, eps, elem, y, codes, scales, rstd,
+                                         None)
+
+
+@pytest.mark.parametrize("hidden", [0, -32, 48, 33, 31])
+def test_bad_hidden(hidden):
+    assert _mxq(hidden=hidden) == EINVAL
+    assert _mxn(hidden=hidden) == EINVAL
+    assert _had(hidden=hidden) == EINVAL
+    assert _rms(hidden=hidden) == EINVAL
+
+
+def test_hidden_above_limit_unsupported():
+    assert _mxq(hidden=mxq.MAX_HIDDEN + 32) == EUNSUP
+    assert _mxn(hidden=mxq.MAX_HIDDEN * 2) == EUNSUP
+
+
+def test_negative_rows_and_bad_elem():
+    assert _mxq(rows=-1) == EINVAL
+    assert _mxn(rows=-5) == EINVAL
+    assert _mxq(elem=2) == EINVAL
+    assert _mxn(elem=-1) == EINVAL
+
+
+def test_zero_rows_is_a_noop_even_without_buffers():
+    assert _mxq(rows=0, x=None, codes=None, scales=None) == OK
+    assert _mxn(rows=0, x=None, codes=None, scales=None) == OK
+    assert _had(rows=0, x=None, codes=None, scales=None) == OK
+    assert _rms(rows=0, x=None, y=None, codes=None, scales=None) == OK
+
+
+def test_null_pointers():
+    assert _mxq(x=None) == EINVAL
+    assert _mxq(codes=None) == EINVAL
+    assert _mxn(scales=None) == EINVAL
+    assert _rms(y=None) == EINVAL
+
+
+def test_misaligned_pointers():
+    assert _mxq(x=MIS) == EALIGN
+    assert _mxq(codes=MIS) == EALIGN
+    assert _mxn(g=MIS) == EALIGN
+    assert _mxn(rrms=A16 + 2) == EALIGN
+    assert _rms(y=MIS) == EALIGN
+    assert _rms(rstd=A16 + 1) == EALIGN
+
+
+@pytest.mark.parametrize("p", [0, 3, -1])
+def test_bad_p(p):
+    assert _mxn(p=p) == EINVAL
+    assert _had(p=p) == EINVAL
+
+
+@pytest.mark.parametrize("c", [-1.0, math.nan, math.inf])
+def test_bad_c(c):
+    assert _mxn(c=c) == EINVAL
+
+
+@pytest.mark.parametrize("had", [0, 8, 64, 17])
+def test_bad_had(had):
+    assert _had(had=had) == EINVAL
+
+
+@pytest.mark.parametrize("eps", [-1e-6, math.nan, math.inf])
+def test_bad_eps(eps):
+    assert _rms(eps=eps) == EINVAL
+
+
+def test_python_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mxq.mxnorm_fwd(x)          # host tensor
+    with pytest.raises(TypeError):
+        mxq.mx_quant(torch.zeros((4, 64), dtype=torch.float32))

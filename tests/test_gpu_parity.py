@@ -1,0 +1,233 @@
+"""GPU parity: libmxnorm.so (through its C ABI) against the CPU oracle, on
+the same seeded inputs.  Run on an MI355X with ``pytest -m gpu``.
+
+Bars (see tests/parity.py): E8M0 scales byte-equal and rho bit-equal always;
+MXNorm / mx_quant / Hadamard element codes are required to be identical (the
+acceptance bar allows one step on 0.01% of elements; these kernels are held
+to zero).  The two-pass baseline accumulates its sum of squares in fp32 on
+the GPU and in fp64 in the oracle, so it is held to: rstd rel <= 1e-5, bf16 y
+within one bf16 ulp, codes within one step on <= 0.01% of elements, scales
+differing on <= 0.01% of blocks and then by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_quantised_tensor_amd as mxq
+import oracle as O
+from mx_quantised_tensor_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+C_DEF = {1: float.fromhex("0x1.b16c5ep+0"), 2: float.fromhex("0x1.c1ed54p+0")}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    mxq.lib()
+    yield
+
+
+def _run_mxnorm(xb, gb, p, c, elem, had=0):
+    x = P.to_device_bf16(xb)
+    g = None if gb is None else P.to_device_bf16(gb)
+    if had:
+        codes, scales, rho = mxq.mxnorm_hadamard_fwd(x, g, p=p, c=c, had=had, elem=elem)
+    else:
+        codes, scales, rho = mxq.mxnorm_fwd(x, g, p=p, c=c, elem=elem)
+    torch.cuda.synchronize()
+    return P.from_device(codes), P.from_device(scales), P.from_device(rho)
+
+
+def _check_mxnorm(xb, gb, p, c, elem, had=0, what=""):
+    gc, gs, gr = _run_mxnorm(xb, gb, p, c, elem, had)
+    if had:
+        oc, os_, orr = O.mxnorm_hadamard_fwd(xb, gb, p, c, had, elem)
+    else:
+        oc, os_, orr = O.mxnorm_fwd(xb, gb, p, c, elem)
+    P.assert_rho_equal(gr, orr, what)
+    P.assert_scales_equal(gs, os_, what)
+    P.assert_codes(gc, oc, os_, elem, exact=True, what=what)
+
+
+def _bits(a):
+    return W.to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+# ------------------------------------------------------------------- mx_quant
+
+@pytest.mark.parametrize("elem", [0, 1])
+@pytest.mark.parametrize("hidden", [32, 96, 768, 4096, 4128, 32768])
+@pytest.mark.parametrize("rows", [1, 3, 130])
+def test_mx_quant_shapes(elem, hidden, rows):
+    xb, _ = W.generate(rows, hidden, "t3", seed=hidden + rows)
+    codes, scales = mxq.mx_quant(P.to_device_bf16(xb), elem=elem)
+    torch.cuda.synchronize()
+    oc, os_ = O.mx_quant(xb, elem)
+    P.assert_scales_equal(P.from_device(scales), os_, "mx_quant")
+    P.assert_codes(P.from_device(codes), oc, os_, elem, exact=True, what="mx_quant")
+
+
+def _edge_matrix():
+    rng = np.random.default_rng(99)
+    rows = []
+    rows.append(np.zeros(64))                                   # zeros
+    rows.append(-np.zeros(64))                                  # negative zeros
+    rows.append(rng.standard_normal(64) * 1e-39)                # bf16 subnormals
+    rows.append(rng.standard_normal(64) * 1e38)                 # near the top of bf16
+    r = rng.standard_normal(64); r[5] = np.inf; rows.append(r)  # Inf in block 0
+    r = rng.standard_normal(64); r[40] = np.nan; rows.append(r) # NaN in block 1
+    # saturation: block max 1.9375 * 2^k -> 496 after the scale, clamps to 448
+    r = rng.uniform(-1, 1, 64); r[0] = 1.9375; r[33] = -1.96875 * 1024; rows.append(r)
+    # ties: values on E4M3 midpoints after scaling by 2^(0-8)
+    r = np.array([1.0] + [(2 ** -8) * (m + 0.5) / 8 * 2 ** 1 for m in range(31)] +
+                 [1.0] + [(2 ** -5) * (1 + (m % 8 + 0.5) / 8) for m in range(31)])
+    rows.append(r)
+    rows.append(np.full(64, 3.0))
+    rows.append(np.where(np.arange(64) % 2 == 0, 6.5, -0.25))  # E2M1 saturation and ties
+    return _bits(np.array(rows))
+
+
+@pytest.mark.parametrize("elem", [0, 1])
+def test_mx_quant_edge_values(elem):
+    xb = _edge_matrix()
+    codes, scales = mxq.mx_quant(P.to_device_bf16(xb), elem=elem)
+    torch.cuda.synchronize()
+    oc, os_ = O.mx_quant(xb, elem)
+    P.assert_scales_equal(P.from_device(scales), os_, "mx_quant edge")
+    P.assert_codes(P.from_device(codes), oc, os_, elem, exact=True, what="mx_quant edge")
+
+
+# ------------------------------------------------------------------ MXNorm
+
+@pytest.mark.parametrize("cfg,p", [(1, 2), (2, 1), (2, 2), (3, 2), (4, 2)])
+def test_mxnorm_workloads_full(cfg, p):
+    w = W.WORKLOADS[cfg]
+    xb, gb = W.workload_inputs(cfg)
+    print("workload", w.name, "p", p, flush=True)
+    _check_mxnorm(xb, gb, p, C_DEF[p], w.elem, w.had, what=w.name)
+
+
+@pytest.mark.parametrize("hidden", [32, 64, 96, 160, 512, 768, 1056, 2048, 4096, 4128, 8192,
+                                    12288, 16384, 32768])
+@pytest.mark.parametrize("elem", [0, 1])
+def test_mxnorm_shapes(hidden, elem):
+    rows = 67 if hidden <= 8192 else 9
+    xb, gb = W.generate(rows, hidden, "rowscale", seed=hidden * 3 + elem)
+    for p in (1, 2):
+        _check_mxnorm(xb, gb, p, C_DEF[p], elem, what="D=%d p=%d" % (hidden, p))
+        _check_mxnorm(xb, None, p, 1.25, elem, what="D=%d p=%d no gamma" % (hidden, p))
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 5, 255, 257])
+def test_mxnorm_ragged_row_counts(rows):
+    xb, gb = W.generate(rows, 2048, "outlier", seed=rows)
+    _check_mxnorm(xb, gb, 2, C_DEF[2], 0, what="rows=%d" % rows)
+
+
+def _edge_rows(hidden):
+    rng = np.random.default_rng(7)
+    base = rng.standard_normal(hidden)
+    rows = [np.zeros(hidden), -np.zeros(hidden), base * 1e-39, base * 3e37, base * 1e-30]
+    r = base.copy(); r[3] = np.nan; rows.append(r)
+    r = base.copy(); r[hidden - 1] = -np.inf; rows.append(r)
+    r = np.zeros(hidden); r[0] = 1.0; rows.append(r)
+    r = np.zeros(hidden); r[hidden // 2] = 2.0 ** -124; rows.append(r)   # large rho
+    r = np.full(hidden, 1.5 * 2.0 ** 126); rows.append(r)               # rho near 2^-127
+    r = base * 2.0 ** 100; r[::32] = 3e38; rows.append(r)
+    return _bits(np.array(rows))
+
+
+@pytest.mark.parametrize("elem", [0, 1])
+@pytest.mark.parametrize("p", [1, 2])
+@pytest.mark.parametrize("hidden", [64, 4096])
+def test_mxnorm_edge_rows(elem, p, hidden):
+    xb = _edge_rows(hidden)
+    gb = _bits(1 + 0.02 * np.random.default_rng(3).standard_normal(hidden))
+    for c in (0.3, 1.0, C_DEF[p], 3.5, 10.0):  # 0.3: subnormal rho; 10: rho overflow
+        _check_mxnorm(xb, gb, p, c, elem, what="edge c=%g" % c)
+        _check_mxnorm(xb, None, p, c, elem, what="edge no gamma c=%g" % c)
+
+
+def test_mxnorm_default_c_and_optional_rrms():
+    xb, gb = W.generate(64, 4096, "outlier", seed=5)
+    x, g = P.to_device_bf16(xb), P.to_device_bf16(gb)
+    c1, s1, r1 = mxq.mxnorm_fwd(x, g, p=2, c=0.0)
+    c2, s2, r2 = mxq.mxnorm_fwd(x, g, p=2, c=0.0, want_rrms=False)
+    torch.cuda.synchronize()
+    assert r2 is None
+    oc, os_, orr = O.mxnorm_fwd(xb, gb, 2, C_DEF[2], 0)
+    P.assert_rho_equal(P.from_device(r1), orr)
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+    P.assert_codes(P.from_device(c1), oc, os_, 0)
+
+
+def test_mxnorm_deterministic_and_side_stream():
+    xb, gb = W.workload_inputs(2)
+    x, g = P.to_device_bf16(xb), P.to_device_bf16(gb)
+    a = mxq.mxnorm_fwd(x, g, p=2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        b = mxq.mxnorm_fwd(x, g, p=2, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------ Hadamard variant
+
+@pytest.mark.parametrize("had", [16, 32])
+@pytest.mark.parametrize("elem", [1, 0])
+@pytest.mark.parametrize("hidden", [32, 96, 768, 4096, 8192])
+def test_hadamard_shapes(had, elem, hidden):
+    xb, gb = W.generate(41, hidden, "outlier", seed=had + hidden)
+    _check_mxnorm(xb, gb, 2, C_DEF[2], elem, had=had, what="H%d D=%d" % (had, hidden))
+    _check_mxnorm(xb, None, 1, 1.5, elem, had=had, what="H%d D=%d no gamma" % (had, hidden))
+
+
+def test_hadamard_workload5_full():
+    w = W.WORKLOADS[5]
+    xb, gb = W.workload_inputs(5)
+    _check_mxnorm(xb, gb, 2, C_DEF[2], w.elem, had=16, what=w.name)
+
+
+@pytest.mark.parametrize("had", [16, 32])
+def test_hadamard_edge_rows(had):
+    xb = _edge_rows(4096)
+    _check_mxnorm(xb, None, 2, 1.0, 1, had=had, what="H%d edge" % had)
+
+
+# ----------------------------------------------------------- two-pass baseline
+
+def _check_baseline(xb, gb, eps, elem, what):
+    x = P.to_device_bf16(xb)
+    g = None if gb is None else P.to_device_bf16(gb)
+    y, codes, scales, rstd = mxq.rmsnorm_mxquant_fwd(x, g, eps=eps, elem=elem)
+    torch.cuda.synchronize()
+    oy, oc, os_, ors = O.rmsnorm_mxquant_fwd(xb, gb, eps, elem)
+    gr = P.from_device(rstd)
+    assert np.max(np.abs(gr.astype(np.float64) / ors - 1)) <= 1e-5, what
+    gy = P.from_device(y.view(torch.int16)).view(np.uint16)
+    dy = np.abs(gy.astype(np.int64) - oy.astype(np.int64))
+    assert dy.max() <= 1, what + ": bf16 y differs by more than one ulp"
+    gs = P.from_device(scales)
+    ds = np.abs(gs.astype(np.int64) - os_.astype(np.int64))
+    assert ds.max() <= 1 and np.count_nonzero(ds) <= max(1, 1e-4 * ds.size), what
+    P.assert_codes(P.from_device(codes), oc, os_, elem, exact=False, what=what)
+
+
+def test_baseline_workload2_full():
+    xb, gb = W.workload_inputs(2)
+    _check_baseline(xb, gb, 1e-5, 0, "two-pass C2")
+
+
+@pytest.mark.parametrize("hidden", [32, 96, 768, 4096, 4128, 16384])
+@pytest.mark.parametrize("elem", [0, 1])
+def test_baseline_shapes(hidden, elem):
+    xb, gb = W.generate(33, hidden, "rowscale", seed=hidden + 11)
+    _check_baseline(xb, gb, 1e-5, elem, "two-pass D=%d" % hidden)
+    _check_baseline(xb, None, 0.0, elem, "two-pass D=%d no gamma" % hidden)
