@@ -1,0 +1,290 @@
+"""Benchmark of the MXNorm forward hot path on one MI355X.
+
+A step is one mxnorm_fwd call (p = 2, E4M3 elements, bf16 gain) over the
+16384 x 4096 bf16 activation matrix (Llama-3 8B hidden size, 4 x 4096 tokens,
+per-row log-normal scale times outlier-Gaussian channels).  Inputs are
+synthetic and resident in HBM before timing starts; R distinct input/output
+buffer sets are rotated so that the 256 MB Infinity Cache cannot serve a step
+from the previous one.  Steps are launched back to back through the C ABI on
+the current stream; one HIP event pair brackets the K timed steps.
+
+Printed: one JSON line with the achieved algorithmic HBM throughput (GB/s),
+a roofline object for the kernel, the CPU oracle timed on the host as a
+reference baseline, and context figures (the two-pass RMSNorm + MX cast
+baseline, the other workloads, a rotated 1 GiB device copy).
+
+`python bench.py --counters` only runs the headline kernel and a 256 MiB
+device copy (the calibration for HBM byte counters) for rocprofv3 --pmc.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
+HEADLINE = 3                     # workload number of the headline line
+METRIC = "MXNorm fwd HBM GB/s (% of MI355X peak), hidden=4096, 16k rows bf16"
+KERNEL_SOURCES = ["mx_quantised_tensor_amd/csrc/mxnorm_kernels.hip",
+                  "mx_quantised_tensor_amd/csrc/mx_device.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "mxnorm_fwd_16384x4096_e4m3_pmc.txt")
+C_P2 = float.fromhex("0x1.c1ed54p+0")  # the library's default c(2, 32)
+
+
+def algorithmic_bytes(rows, hidden, elem, gamma=True, with_rrms=True):
+    """Bytes the operation must move: read x (2 B/elem) and gamma (2 B per
+    column), write codes (1 or 0.5 B/elem), scales (1 B per 32) and rho
+    (4 B per row)."""
+    code_bytes = rows * hidden if elem == 0 else rows * hidden // 2
+    return (2 * rows * hidden + (2 * hidden if gamma else 0) + code_bytes
+            + rows * (hidden // 32) + (4 * rows if with_rrms else 0))
+
+
+def two_pass_bytes(rows, hidden, elem):
+    """RMSNorm pass (read x, gamma; write bf16 y, rstd) + MX cast of y."""
+    code_bytes = rows * hidden if elem == 0 else rows * hidden // 2
+    return (2 * rows * hidden + 2 * hidden + 2 * rows * hidden + 4 * rows
+            + 2 * rows * hidden + code_bytes + rows * (hidden // 32))
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    valid only while the kernel sources are unchanged since it was taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--buffers", type=int, default=6, help="rotated buffer sets")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the headline kernel and a calibration copy (for --pmc)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MXNorm path is per-row independent and this "
+              "build runs on a single MI355X; --gpus %d is not supported." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mx_quantised_tensor_amd as mxq
+    from mx_quantised_tensor_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    L = mxq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def device_sets(xb, gb, elem, nsets, two_pass=False):
+        rows, hidden = xb.shape
+        x0 = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        g = torch.from_numpy(gb.view(np.int16)).to(dev).view(torch.bfloat16)
+        sets = []
+        for i in range(nsets):
+            x = x0 if i == 0 else x0.clone()
+            ccols = hidden if elem == 0 else hidden // 2
+            s = dict(x=x, codes=torch.empty((rows, ccols), dtype=torch.uint8, device=dev),
+                     scales=torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev),
+                     rrms=torch.empty((rows,), dtype=torch.float32, device=dev))
+            if two_pass:
+                s["y"] = torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)
+            sets.append(s)
+        return g, sets
+
+    # Calls through the C ABI with the pointers resolved once, so the host
+    # keeps ahead of the GPU and the steps run back to back.
+    def mxnorm_calls(sets, g, rows, hidden, p, elem, had=0):
+        calls = []
+        for s in sets:
+            a = (s["x"].data_ptr(), g.data_ptr(), rows, hidden, p, 0.0)
+            o = (s["codes"].data_ptr(), s["scales"].data_ptr(), s["rrms"].data_ptr(), sp)
+            if had:
+                calls.append(lambda a=a, o=o: L.mxnorm_hadamard_fwd(*a, had, elem, *o))
+            else:
+                calls.append(lambda a=a, o=o: L.mxnorm_fwd(*a, elem, *o))
+        return calls
+
+    def run(calls, n):
+        for i in range(n):
+            rc = calls[i % len(calls)]()
+            if rc != 0:
+                raise RuntimeError(mxq.status_str(rc))
+
+    def time_region(calls, steps, warmup):
+        """Wall time and GPU time (one event pair on the launch stream) of
+        `steps` back-to-back calls, synchronised on both sides."""
+        run(calls, warmup)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run(calls, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1) * 1e-3
+
+    def launch_spread(calls, n):
+        """Per-launch event durations (context: spread across launches)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            run([calls[i % len(calls)]], 1)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+
+    # ---------------------------------------------------------------- headline
+    w = W.WORKLOADS[HEADLINE]
+    xb, gb = W.workload_inputs(HEADLINE)
+    rows, hidden = xb.shape
+    g, sets = device_sets(xb, gb, w.elem, args.buffers)
+    calls = mxnorm_calls(sets, g, rows, hidden, 2, w.elem)
+    nbytes = algorithmic_bytes(rows, hidden, w.elem)
+
+    if args.counters:
+        run(calls, 20)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("counters run: 20 x mxnorm_fwd %dx%d, 20 x 256 MiB copy" % (rows, hidden))
+        return
+
+    wall, gpu_s = time_region(calls, args.steps, args.warmup)
+    value = nbytes * args.steps / wall / 1e9
+    kern_s = gpu_s / args.steps
+    achieved = nbytes / kern_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": read_traffic()}
+    spread = launch_spread(calls, 60)
+    extras = {"algorithmic_bytes_per_launch": nbytes,
+              "kernel_us_mean_timed_region": round(kern_s * 1e6, 3),
+              "single_launch_event_us_p10_p50_p90": [
+                  round(float(np.percentile(spread, q)) * 1e6, 2) for q in (10, 50, 90)],
+              "rows_per_s": round(rows * args.steps / wall, 1),
+              "pct_of_peak_wall": round(100 * value / PEAK_HBM_GBS, 2),
+              "buffer_sets": args.buffers,
+              "kernel_source_hash": kernel_hash()}
+
+    if not args.no_extras:
+        # two-pass baseline on the same workload
+        del sets, calls
+        torch.cuda.empty_cache()
+        g2, sets2 = device_sets(xb, gb, w.elem, max(2, args.buffers // 2), two_pass=True)
+        tp_calls = []
+        for s in sets2:
+            a = (s["x"].data_ptr(), g2.data_ptr(), rows, hidden, 1e-5, w.elem, s["y"].data_ptr(),
+                 s["codes"].data_ptr(), s["scales"].data_ptr(), s["rrms"].data_ptr(), sp)
+            tp_calls.append(lambda a=a: L.rmsnorm_mxquant_fwd(*a))
+        n2 = max(30, args.steps // 4)
+        wall2, gpu2 = time_region(tp_calls, n2, 10)
+        extras["two_pass_us_per_call"] = round(gpu2 / n2 * 1e6, 3)
+        extras["speedup_vs_two_pass"] = round((gpu2 / n2) / kern_s, 3)
+        extras["two_pass_algorithmic_GBps"] = round(two_pass_bytes(rows, hidden, w.elem)
+                                                    / (gpu2 / n2) / 1e9, 1)
+        del sets2, tp_calls
+        # Context: a plain device-to-device copy (torch's copy kernel) of 1 GiB,
+        # two buffer pairs rotated so the Infinity Cache cannot serve it.
+        cbytes = 1 << 30
+        pairs = [(torch.empty(cbytes, dtype=torch.uint8, device=dev),
+                  torch.empty(cbytes, dtype=torch.uint8, device=dev)) for _ in range(2)]
+        for i in range(4):
+            pairs[i % 2][1].copy_(pairs[i % 2][0])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(10):
+            pairs[i % 2][1].copy_(pairs[i % 2][0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extras["device_copy_GBps_1GiB"] = round(2 * cbytes * 10 / (e0.elapsed_time(e1) * 1e-3)
+                                                / 1e9, 1)
+        del pairs
+        torch.cuda.empty_cache()
+
+        # the other workloads (context; the headline is workload 3)
+        others = {}
+        for cfg in (1, 2, 4, 5):
+            wc = W.WORKLOADS[cfg]
+            xc, gc = W.workload_inputs(cfg)
+            r, d = xc.shape
+            nset = 2 if r * d <= 256 * 1024 else max(2, args.buffers // 2)
+            gdev, sc = device_sets(xc, gc, wc.elem, nset)
+            for p in wc.ps:
+                cl = mxnorm_calls(sc, gdev, r, d, p, wc.elem, wc.had)
+                nst = max(30, args.steps // 4)
+                wl, gt = time_region(cl, nst, 5)
+                b = algorithmic_bytes(r, d, wc.elem)
+                others["%s_p%d" % (wc.name, p)] = {
+                    "kernel_us_mean": round(gt / nst * 1e6, 3),
+                    "GBps_kernel": round(b * nst / gt / 1e9, 1),
+                    "GBps_wall": round(b * nst / wl / 1e9, 1)}
+            del sc
+            torch.cuda.empty_cache()
+        extras["other_workloads"] = others
+
+    # ------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        O.lib()
+        reps = []
+        for _ in range(2):
+            t0 = time.perf_counter()
+            O.mxnorm_fwd(xb, gb, 2, C_P2, w.elem)
+            reps.append(time.perf_counter() - t0)
+        t = min(reps)
+        cpu = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s",
+               "cores": O.max_threads(), "kind": "oracle",
+               "sample": "the full 16384x4096 headline matrix, best of 2 runs "
+                         "(%.2f s each), OpenMP over rows" % t}
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall / args.steps * 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "rows": rows, "hidden": hidden, "p": 2,
+                      "elem": "e4m3", "gamma": True, "block": 32,
+                      "inputs": "bf16 N(0,1), 1% outlier channels x20, per-row lognormal "
+                                "scale (sigma 1), seed 3"},
+           "roofline": roofline, "cpu_baseline": cpu, "extras": extras}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,9 +44,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// DPP read with bound_ctrl and a zero `old`, the form the compiler folds
+// into the consuming VALU instruction (e.g. v_max_u32_dpp).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp0_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<kDppQuadSwap1>(v));
-  v = max(v, dpp_u32<kDppQuadSwap2>(v));
+  v = max(v, dpp0_u32<kDppQuadSwap1>(v));
+  v = max(v, dpp0_u32<kDppQuadSwap2>(v));
   return v;
 }
 

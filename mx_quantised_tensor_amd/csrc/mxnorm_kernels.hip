@@ -7,10 +7,16 @@
 //   [P3] MXFP4 pre-training on AMD MI355X (gist.science summary),
 //        "Metodologia", "Hallazgos" 2 (deterministic H16 / H32 rotation).
 //
-// All kernels are HBM-bandwidth bound streaming codecs: no MFMA (no dense
-// contraction exists on this path), 16-byte loads and stores per lane, a
-// row held in VGPRs between its statistic and its cast, and workgroups
-// assigned to XCDs in contiguous row ranges.
+// Every kernel here is an HBM-bandwidth-bound streaming codec: there is no
+// dense contraction on this path, so no MFMA.  The design points are
+//   * a lane owns 8 consecutive bf16 (one 16-byte load); a quad of lanes owns
+//     a 32-element MX block, so block reductions are two quad DPP steps;
+//   * one wavefront owns a whole row (hidden <= 4096) and keeps it in VGPRs
+//     between the row statistic and the cast -- no barriers, ~60 VGPRs, 8
+//     waves per SIMD to keep HBM requests in flight;
+//   * x is loaded and the codes stored non-temporally (each byte is touched
+//     once); the gain is requested with the row and comes from L2;
+//   * workgroups are renumbered so that each XCD streams a contiguous range.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,9 +25,8 @@
 
 namespace mxq {
 
-constexpr int kThreads = 256;             // 4 waves per workgroup
-constexpr int kNegExp = -100000;          // exponent of a block outside the row
-constexpr int kNonFinite = 1000;          // exponent marking a NaN/Inf block
+constexpr int kThreads = 256;     // 4 waves per workgroup
+constexpr int kInactive = -256;   // block exponent of a lane past the row end
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
 // XCD (and its L2) works through one contiguous range of rows.
@@ -43,136 +48,276 @@ struct Elem<1> {  // E2M1: largest power of two 2^2 (6 = 1.5 * 2^2)
   static constexpr int kCodeBytesPerLane = 4;
 };
 
+// ---- streaming memory access ----------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int ELEM>
-__device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const float (&y)[8],
-                                            uint32_t e8m0) {
-  if constexpr (ELEM == 0)
-    *reinterpret_cast<uint2*>(dst) = encode8_e4m3(y, e8m0);
-  else
-    *reinterpret_cast<uint32_t*>(dst) = encode8_e2m1(y, e8m0);
+__device__ __forceinline__ void store_codes_stream(uint8_t* __restrict__ dst, const float (&y)[8],
+                                                   uint32_t e8m0) {
+  if constexpr (ELEM == 0) {
+    const uint2 c = encode8_e4m3(y, e8m0);
+    const u32x2_t v = {c.x, c.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(dst));
+  } else {
+    __builtin_nontemporal_store(encode8_e2m1(y, e8m0), reinterpret_cast<uint32_t*>(dst));
+  }
+}
+
+// ---- the MXNorm row statistic ([P1] §2 "Formula"; [P2] abstract) -----------------
+// Block magnitude: mt_k = 2^(e_k + emax) where e_k is the E8M0 exponent the MX
+// cast of x gives block k.  From the bf16 exponent field f of the block
+// absmax, e_k + emax + 127 = max(f, emax) (the E8M0 clamp at -127 included);
+// u = 255 marks a block holding NaN or Inf.
+template <int EMAX>
+__device__ __forceinline__ int block_u(const uint4 v) {
+  const uint32_t m = quad_max_u32(absmax8_bf16_bits(v));
+  return max((int)(m >> 7), EMAX);
+}
+
+// The terms of S = sum_k 2^(40 - p (E1 - u_k)) with p (E1 - u_k) <= 40, as
+// exact doubles: the double whose high word is (1063 - t) << 20 (low word 0)
+// is 2^(40 - t).  S < 2^53, so summing these in fp64 is exact in any order.
+struct PowerSum {
+  int hbase;  // (1063 << 20) - (E1 << pk)
+  int umin;   // E1 - 40/p
+  int pk;     // 20 + (p - 1): (p (E1 - u)) << 20 == (E1 - u) << pk for p in {1, 2}
+  __device__ __forceinline__ PowerSum(int E1, int p_shift) {
+    pk = 20 + p_shift;
+    hbase = (1063 << 20) - (E1 << pk);
+    umin = E1 - (40 >> p_shift);
+  }
+  __device__ __forceinline__ double term(int u) const {
+    return __hiloint2double(u >= umin ? hbase + (u << pk) : 0, 0);
+  }
+};
+
+// rho = fl(c / r) * 2^(40/p - E), r = fl(fl(S)/K) (p = 1) or fl(sqrt(fl(fl(S)/K))),
+// E = E1 - 127.  Each step is one correctly rounded fp32 operation, evaluated in
+// fp64 and rounded once: a double result of +, *, /, sqrt on floats rounds to
+// the correctly rounded float (53 >= 2*24 + 2).  S * (1/K) in fp64 rounds to the
+// same float as S / K: a 24-bit S divided by K <= 2^10 is never within 2^-52 of
+// a float rounding boundary.  E1 == 255 (NaN/Inf in the row) gives NaN.
+__device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, float c,
+                                               double inv_k) {
+  if (E1 >= 255) return __uint_as_float(0x7FC00000u);
+  const float Sf = (float)S;  // exact in fp64 below 2^53; one rounding here
+  const float mu = (float)((double)Sf * inv_k);
+  const float r = p_shift == 0 ? mu : (float)sqrt((double)mu);
+  const float q = (float)((double)c / (double)r);
+  return (float)ldexp((double)q, (40 >> p_shift) - (E1 - 127));
+}
+
+// ---- normalise (+gain), rotate, re-derive the block scale from y, cast ----------
+// ([P1] §2 "Implementacion": scale the values and produce the quantisation
+// scales in the same pass; [P3]: H16 / H32 rotation before the MXFP4 cast.)
+template <int ELEM, bool GAMMA, int HAD>
+__device__ __forceinline__ uint32_t cast_chunk(const uint4 xv, const uint4 gv, float rho,
+                                               int lane, uint8_t* __restrict__ dst) {
+  constexpr int EMAX = Elem<ELEM>::kEmax;
+  float y[8];
+  widen8(xv, y);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = y[i] * rho;
+  if constexpr (GAMMA) {
+    float g[8];
+    widen8(gv, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * g[i];
+  }
+  if constexpr (HAD != 0) {
+    fwht8_inlane(y);
+    fwht8_crosslane<kDppQuadSwap1>(y, (lane & 1) != 0);
+    if constexpr (HAD == 32) fwht8_crosslane<kDppQuadSwap2>(y, (lane & 2) != 0);
+    constexpr float norm = HAD == 16 ? 0.25f : 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * norm;
+  }
+  const uint32_t mb = quad_max_u32(absmax8_f32_bits(y));
+  const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
+  store_codes_stream<ELEM>(dst, y, sb);
+  return sb;
 }
 
 // ----------------------------------------------------------------------------------
-// MXNorm forward ([P1] §2 "Implementacion": absmax per block -> RMS estimate ->
-// scale the values -> quantisation scales, one pass; [P1] §2 "Formula").
-//
-// A row is owned by W waves (4/W rows per workgroup).  Lane `lane` of wave
-// `wir` owns chunk (s*W + wir)*64 + lane of the row at step s (8 bf16 each).
-// Phase 1 keeps the row in VGPRs and reduces the E8M0 exponents of its
-// blocks; phase 2 normalises, rotates (HAD), re-derives the output scales
-// and casts.
+// MXNorm forward, one wave per row (hidden <= 512 * STEPS <= 4096), four rows
+// per workgroup.  Lane `lane` owns chunk s*64 + lane of the row at step s.
+// ----------------------------------------------------------------------------------
+struct WaveArgs {
+  const uint8_t* x;
+  const uint8_t* gamma;
+  int64_t rows;
+  int hidden;
+  int p_shift;   // p - 1
+  float c;
+  double inv_k;  // 1 / K
+  uint8_t* codes;
+  uint8_t* scales;
+  float* rrms;
+  int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
+};
+
+template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+  constexpr int EMAX = Elem<ELEM>::kEmax;
+  constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
+  __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
+  if (row >= a.rows) return;  // whole wave; no barriers in this kernel
+
+  const int nchunk = a.hidden >> 3;
+  const int K = a.hidden >> 5;
+  uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
+  bool act[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int ch = s * kWave + lane;
+    act[s] = FULL || ch < nchunk;  // uniform over each quad (nchunk % 4 == 0)
+    choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;  // clamped: stays in the row
+  }
+
+  const uint8_t* xrow = a.x + row * (int64_t)a.hidden * 2;
+  uint4 v[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + choff[s]);
+  // the gain (L2-resident) is requested with the row, so it has arrived by the
+  // time the row statistic is done
+  uint4 gr[GAMMA ? STEPS : 1];
+  if constexpr (GAMMA) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(a.gamma + choff[s]);
+  } else {
+    gr[0] = make_uint4(0, 0, 0, 0);
+  }
+
+  int u[STEPS];
+  int umax = kInactive;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    int us = block_u<EMAX>(v[s]);
+    if constexpr (!FULL) us = act[s] ? us : kInactive;
+    u[s] = us;
+    umax = max(umax, us);
+  }
+  const int E1 = wave_max_quads(umax);
+
+  float rho;
+  {
+    const PowerSum ps(E1, a.p_shift);
+    double S = 0.0;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) S += ps.term(u[s]);
+    S = wave_sum_quads_f64(S);
+    rho = rho_from_stat(E1, S, a.p_shift, a.c, a.inv_k);
+  }
+  if (a.rrms != nullptr && lane == 0) a.rrms[row] = rho;
+
+  uint8_t* crow = a.codes + row * (int64_t)(ELEM == 0 ? a.hidden : a.hidden / 2);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    if (!FULL && !act[s]) continue;  // quad-uniform; the DPP inside stays in the quad
+    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(
+        v[s], gr[GAMMA ? s : 0], rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
+    reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
+  }
+  // the scale bytes written above are read back by other lanes of the wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint8_t* srow = a.scales + row * K;
+  if (a.scales_dwords) {  // K / 4 <= STEPS * 4 <= 32 dwords: one store per lane
+    if (lane < (K >> 2)) reinterpret_cast<uint32_t*>(srow)[lane] = s_sc[wave][lane];
+  } else {
+#pragma unroll
+    for (int j = 0; j < (STEPS * 16 + kWave - 1) / kWave; ++j) {
+      const int i = j * kWave + lane;
+      if (i < K) srow[i] = reinterpret_cast<const uint8_t*>(s_sc[wave])[i];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// MXNorm forward for wide rows (4096 < hidden <= 32768): a row is owned by W
+// waves (4/W rows per workgroup); the two row reductions cross waves through
+// LDS.  Lane `lane` of wave `wir` owns chunk (s*W + wir)*64 + lane at step s.
 // ----------------------------------------------------------------------------------
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS>
-__global__ __launch_bounds__(kThreads) void k_mxnorm(
-    const uint4* __restrict__ x, const uint4* __restrict__ gamma, int64_t rows, int hidden,
-    int p, float c, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ rrms) {
+__global__ __launch_bounds__(kThreads) void k_mxnorm_wide(const WaveArgs a) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
+  constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   constexpr int RPW = 4 / W;
-  static_assert(W == 1 || W == 2 || W == 4, "waves per row");
+  static_assert(W == 2 || W == 4, "waves per row");
+  __shared__ int s_max[4];
+  __shared__ double s_sum[4];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rslot = wave / W;
   const int wir = wave % W;
   const int64_t row = xcd_remap(blockIdx.x, gridDim.x) * RPW + rslot;
-  const bool row_ok = row < rows;
-  const int nchunk = hidden >> 3;
-  const int K = hidden >> 5;
+  const bool row_ok = row < a.rows;  // waves past the end still join the barriers
+  const int nchunk = a.hidden >> 3;
+  const int K = a.hidden >> 5;
 
-  // ---- load the row (16 B per lane per step) --------------------------------------
+  const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
   uint4 v[STEPS];
   bool act[STEPS];
+  uint32_t choff[STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int ch = (s * W + wir) * kWave + lane;
-    act[s] = row_ok && ch < nchunk;  // uniform over each quad: nchunk % 4 == 0
-    v[s] = act[s] ? x[row * nchunk + ch] : make_uint4(0, 0, 0, 0);
+    act[s] = row_ok && ch < nchunk;
+    choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
+    v[s] = load_stream16(xrow + choff[s]);
   }
 
-  // ---- block exponents e_k + emax, from the bf16 exponent field ------------------
-  int eh[STEPS];
-  int emx = kNegExp;
+  int u[STEPS];
+  int umax = kInactive;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const uint32_t m = quad_max_u32(absmax8_bf16_bits(v[s]));
-    const int e = m >= 0x7F80u ? kNonFinite : max((int)(m >> 7) - 127 - EMAX, -127) + EMAX;
-    eh[s] = act[s] ? e : kNegExp;
-    emx = max(emx, eh[s]);
+    const int us = block_u<EMAX>(v[s]);
+    u[s] = act[s] ? us : kInactive;
+    umax = max(umax, u[s]);
   }
-  emx = wave_max_quads(emx);
-  __shared__ int s_max[4];
-  __shared__ double s_sum[4];
-  if constexpr (W > 1) {
-    if (lane == 0) s_max[wave] = emx;
-    __syncthreads();
-    emx = s_max[rslot * W];
+  umax = wave_max_quads(umax);
+  if (lane == 0) s_max[wave] = umax;
+  __syncthreads();
+  int E1 = s_max[rslot * W];
 #pragma unroll
-    for (int w = 1; w < W; ++w) emx = max(emx, s_max[rslot * W + w]);
-  }
-  const int E = emx;
+  for (int w = 1; w < W; ++w) E1 = max(E1, s_max[rslot * W + w]);
 
-  // ---- power sum S = sum 2^(40 - p (E - eh)), exact in fp64 ---------------------
+  const PowerSum ps(E1, a.p_shift);
   double S = 0.0;
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int t = p * (E - eh[s]);
-    if (t <= 40) S += __longlong_as_double((int64_t)(1023 + 40 - t) << 52);
-  }
+  for (int s = 0; s < STEPS; ++s) S += ps.term(u[s]);
   S = wave_sum_quads_f64(S);
-  if constexpr (W > 1) {
-    if (lane == 0) s_sum[wave] = S;
-    __syncthreads();
-    S = s_sum[rslot * W];
+  if (lane == 0) s_sum[wave] = S;
+  __syncthreads();
+  S = s_sum[rslot * W];
 #pragma unroll
-    for (int w = 1; w < W; ++w) S += s_sum[rslot * W + w];
-  }
+  for (int w = 1; w < W; ++w) S += s_sum[rslot * W + w];
+  const float rho = rho_from_stat(E1, S, a.p_shift, a.c, a.inv_k);
+  if (a.rrms != nullptr && row_ok && wir == 0 && lane == 0) a.rrms[row] = rho;
 
-  // ---- rho = fl(c / r) * 2^(40/p - E) -------------------------------------------
-  // Each step is one correctly rounded fp32 operation.  It is evaluated in
-  // fp64 and rounded once to fp32, which gives the same value: for +, /, sqrt
-  // a double result rounded to float is the correctly rounded float result
-  // (53 >= 2*24 + 2).
-  float rho;
-  if (E >= kNonFinite) {
-    rho = __uint_as_float(0x7FC00000u);
-  } else {
-    const float Sf = (float)S;  // S < 2^53 is exact in fp64; one rounding here
-    const float mu = (float)((double)Sf / (double)K);
-    const float r = p == 1 ? mu : (float)sqrt((double)mu);
-    const float q = (float)((double)c / (double)r);
-    rho = (float)ldexp((double)q, 40 / p - E);
-  }
-  if (rrms != nullptr && row_ok && wir == 0 && lane == 0) rrms[row] = rho;
-
-  // ---- normalise, rotate, re-derive scales, cast --------------------------------
-  const int64_t crow = row * (int64_t)(ELEM == 0 ? hidden : hidden / 2);
+  uint8_t* crow = a.codes + row * (int64_t)(ELEM == 0 ? a.hidden : a.hidden / 2);
+  uint8_t* srow = a.scales + row * K;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    if (!act[s]) continue;  // quad-uniform; DPP below stays inside the quad
+    if (!act[s]) continue;
     const int ch = (s * W + wir) * kWave + lane;
-    float y[8];
-    widen8(v[s], y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = y[i] * rho;
-    if constexpr (GAMMA) {
-      float g[8];
-      widen8(gamma[ch], g);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = y[i] * g[i];
-    }
-    if constexpr (HAD != 0) {
-      fwht8_inlane(y);
-      fwht8_crosslane<kDppQuadSwap1>(y, (lane & 1) != 0);
-      if constexpr (HAD == 32) fwht8_crosslane<kDppQuadSwap2>(y, (lane & 2) != 0);
-      constexpr float norm = HAD == 16 ? 0.25f : 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = y[i] * norm;
-    }
-    const uint32_t mb = quad_max_u32(absmax8_f32_bits(y));
-    const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
-    store_codes<ELEM>(codes + crow + (int64_t)ch * Elem<ELEM>::kCodeBytesPerLane, y, sb);
-    if ((lane & 3) == 0) scales[row * K + (ch >> 2)] = (uint8_t)sb;
+    const uint4 gv = GAMMA ? *reinterpret_cast<const uint4*>(a.gamma + choff[s])
+                           : make_uint4(0, 0, 0, 0);
+    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(v[s], gv, rho, lane,
+                                                     crow + (uint32_t)ch * (uint32_t)CB);
+    if ((lane & 3) == 0) srow[ch >> 2] = (uint8_t)sb;
   }
 }
 
@@ -186,21 +331,22 @@ __global__ __launch_bounds__(kThreads) void k_mx_quant(const uint4* __restrict__
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
-  const int64_t nwg = gridDim.x;
-  const int64_t ch = xcd_remap(blockIdx.x, nwg) * kThreads + threadIdx.x;
+  const int64_t ch = xcd_remap(blockIdx.x, gridDim.x) * kThreads + threadIdx.x;
   if (ch >= nchunks) return;  // nchunks % 4 == 0: quads stay whole
   const uint4 v = x[ch];
   const uint32_t m = quad_max_u32(absmax8_bf16_bits(v));
   const uint32_t sb = e8m0_from_expfield<EMAX>(m >> 7);
   float y[8];
   widen8(v, y);
-  store_codes<ELEM>(codes + ch * Elem<ELEM>::kCodeBytesPerLane, y, sb);
+  store_codes_stream<ELEM>(codes + ch * Elem<ELEM>::kCodeBytesPerLane, y, sb);
   if ((threadIdx.x & 3) == 0) scales[ch >> 2] = (uint8_t)sb;
 }
 
 // ----------------------------------------------------------------------------------
 // RMSNorm, pass 1 of the two-pass baseline ([P1] §1): full-width fp32 sum of
-// squares, rstd = 1/sqrt(mean + eps), bf16 y written to memory.
+// squares, rstd = 1/sqrt(mean + eps), bf16 y written to memory.  Same row
+// layout as the MXNorm kernels (W waves per row); y is stored with ordinary
+// stores so that pass 2 may find it in the Infinity Cache.
 // ----------------------------------------------------------------------------------
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -211,8 +357,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <bool GAMMA, int W, int STEPS>
-__global__ __launch_bounds__(kThreads) void k_rmsnorm(const uint4* __restrict__ x,
-                                                       const uint4* __restrict__ gamma,
+__global__ __launch_bounds__(kThreads) void k_rmsnorm(const uint8_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ gamma,
                                                        int64_t rows, int hidden, float eps,
                                                        uint4* __restrict__ y,
                                                        float* __restrict__ rstd) {
@@ -223,27 +369,41 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm(const uint4* __restrict__ 
   const int wir = wave % W;
   const int64_t row = xcd_remap(blockIdx.x, gridDim.x) * RPW + rslot;
   const bool row_ok = row < rows;
+  if constexpr (W == 1) {
+    if (!row_ok) return;  // whole wave; no barriers when a wave owns its row
+  }
   const int nchunk = hidden >> 3;
 
-  uint4 v[STEPS];
+  const uint8_t* xrow = x + (row_ok ? row : 0) * (int64_t)hidden * 2;
+  uint4 v[STEPS], gr[GAMMA ? STEPS : 1];
   bool act[STEPS];
+  uint32_t choff[STEPS];
   float ss = 0.0f;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int ch = (s * W + wir) * kWave + lane;
     act[s] = row_ok && ch < nchunk;
-    v[s] = act[s] ? x[row * nchunk + ch] : make_uint4(0, 0, 0, 0);
+    choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
+    v[s] = load_stream16(xrow + choff[s]);
+  }
+  if constexpr (GAMMA) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(gamma + choff[s]);
+  } else {
+    gr[0] = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     float f[8];
     widen8(v[s], f);
+    if (act[s]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+      for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+    }
   }
   ss = wave_sum_f32(ss);
-  __shared__ float s_sum[4];
   if constexpr (W > 1) {
+    __shared__ float s_sum[4];
     if (lane == 0) s_sum[wave] = ss;
     __syncthreads();
     ss = s_sum[rslot * W];
@@ -253,6 +413,7 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm(const uint4* __restrict__ 
   const float rs = 1.0f / __builtin_sqrtf(ss / (float)hidden + eps);
   if (rstd != nullptr && row_ok && wir == 0 && lane == 0) rstd[row] = rs;
 
+  uint4* yrow = y + row * (int64_t)nchunk;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     if (!act[s]) continue;
@@ -263,12 +424,12 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm(const uint4* __restrict__ 
     for (int i = 0; i < 8; ++i) f[i] = f[i] * rs;
     if constexpr (GAMMA) {
       float g[8];
-      widen8(gamma[ch], g);
+      widen8(gr[s], g);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * g[i];
     }
-    y[row * nchunk + ch] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    yrow[ch] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
 }
 
@@ -291,36 +452,63 @@ RowShape pick_row_shape(int hidden) {
   return {0, 0};
 }
 
+WaveArgs wave_args(const MxnormArgs& m) {
+  WaveArgs a;
+  a.x = static_cast<const uint8_t*>(m.x);
+  a.gamma = static_cast<const uint8_t*>(m.gamma);
+  a.rows = m.rows;
+  a.hidden = m.hidden;
+  a.p_shift = m.p - 1;
+  a.c = m.c;
+  a.inv_k = 1.0 / (double)(m.hidden / 32);
+  a.codes = m.codes;
+  a.scales = m.scales;
+  a.rrms = m.rrms;
+  a.scales_dwords = ((m.hidden / 32) % 4 == 0) && (((uintptr_t)m.scales & 3) == 0);
+  return a;
+}
+
+template <int ELEM, bool GAMMA, int HAD, int STEPS>
+hipError_t launch_wave(const MxnormArgs& m) {
+  const WaveArgs a = wave_args(m);
+  const dim3 grid((unsigned)((m.rows + 3) / 4));
+  if (m.hidden == 512 * STEPS)
+    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, true>), grid, dim3(kThreads), 0,
+                       (hipStream_t)m.stream, a);
+  else
+    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, false>), grid, dim3(kThreads), 0,
+                       (hipStream_t)m.stream, a);
+  return hipGetLastError();
+}
+
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS>
-hipError_t launch_mxnorm_t(const MxnormArgs& a) {
-  const int64_t rpw = 4 / W;
-  const int64_t grid = (a.rows + rpw - 1) / rpw;
-  hipLaunchKernelGGL((k_mxnorm<ELEM, GAMMA, HAD, W, STEPS>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, (hipStream_t)a.stream,
-                     static_cast<const uint4*>(a.x), static_cast<const uint4*>(a.gamma), a.rows,
-                     a.hidden, a.p, a.c, a.codes, a.scales, a.rrms);
+hipError_t launch_wide(const MxnormArgs& m) {
+  const WaveArgs a = wave_args(m);
+  const dim3 grid((unsigned)((m.rows + (4 / W) - 1) / (4 / W)));
+  hipLaunchKernelGGL((k_mxnorm_wide<ELEM, GAMMA, HAD, W, STEPS>), grid, dim3(kThreads), 0,
+                     (hipStream_t)m.stream, a);
   return hipGetLastError();
 }
 
 template <int ELEM, bool GAMMA, int HAD>
-hipError_t launch_mxnorm_shape(const MxnormArgs& a) {
-  const RowShape r = pick_row_shape(a.hidden);
-  if (r.waves == 1 && r.steps == 1) return launch_mxnorm_t<ELEM, GAMMA, HAD, 1, 1>(a);
-  if (r.waves == 1 && r.steps == 2) return launch_mxnorm_t<ELEM, GAMMA, HAD, 1, 2>(a);
-  if (r.waves == 1 && r.steps == 4) return launch_mxnorm_t<ELEM, GAMMA, HAD, 1, 4>(a);
-  if (r.waves == 1 && r.steps == 8) return launch_mxnorm_t<ELEM, GAMMA, HAD, 1, 8>(a);
-  if (r.waves == 2 && r.steps == 8) return launch_mxnorm_t<ELEM, GAMMA, HAD, 2, 8>(a);
-  if (r.waves == 4 && r.steps == 8) return launch_mxnorm_t<ELEM, GAMMA, HAD, 4, 8>(a);
-  if (r.waves == 4 && r.steps == 16) return launch_mxnorm_t<ELEM, GAMMA, HAD, 4, 16>(a);
+hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
+  const RowShape r = pick_row_shape(m.hidden);
+  if (r.waves == 1 && r.steps == 1) return launch_wave<ELEM, GAMMA, HAD, 1>(m);
+  if (r.waves == 1 && r.steps == 2) return launch_wave<ELEM, GAMMA, HAD, 2>(m);
+  if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, 4>(m);
+  if (r.waves == 1 && r.steps == 8) return launch_wave<ELEM, GAMMA, HAD, 8>(m);
+  if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, 2, 8>(m);
+  if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, 4, 8>(m);
+  if (r.waves == 4 && r.steps == 16) return launch_wide<ELEM, GAMMA, HAD, 4, 16>(m);
   return hipErrorInvalidValue;
 }
 
 template <int ELEM, bool GAMMA>
-hipError_t launch_mxnorm_had(const MxnormArgs& a) {
-  switch (a.had) {
-    case 0: return launch_mxnorm_shape<ELEM, GAMMA, 0>(a);
-    case 16: return launch_mxnorm_shape<ELEM, GAMMA, 16>(a);
-    case 32: return launch_mxnorm_shape<ELEM, GAMMA, 32>(a);
+hipError_t launch_mxnorm_had(const MxnormArgs& m) {
+  switch (m.had) {
+    case 0: return launch_mxnorm_shape<ELEM, GAMMA, 0>(m);
+    case 16: return launch_mxnorm_shape<ELEM, GAMMA, 16>(m);
+    case 32: return launch_mxnorm_shape<ELEM, GAMMA, 32>(m);
     default: return hipErrorInvalidValue;
   }
 }
@@ -331,8 +519,8 @@ hipError_t launch_rmsnorm_t(const void* x, const void* gamma, int64_t rows, int 
   const int64_t rpw = 4 / W;
   const int64_t grid = (rows + rpw - 1) / rpw;
   hipLaunchKernelGGL((k_rmsnorm<GAMMA, W, STEPS>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, static_cast<const uint4*>(x),
-                     static_cast<const uint4*>(gamma), rows, hidden, eps,
+                     (hipStream_t)stream, static_cast<const uint8_t*>(x),
+                     static_cast<const uint8_t*>(gamma), rows, hidden, eps,
                      static_cast<uint4*>(y), rstd);
   return hipGetLastError();
 }
