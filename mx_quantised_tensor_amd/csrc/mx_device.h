@@ -209,7 +209,9 @@ __device__ __forceinline__ void fwht8_crosslane(float (&y)[8], bool upper) {
   const uint32_t flip = upper ? 0x80000000u : 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float partner = dpp_f32<CTRL>(y[j]);
+    // bound_ctrl + zero `old`: the move folds into v_add_f32_dpp
+    const float partner =
+        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y[j]), CTRL, 0xF, 0xF, true));
     y[j] = partner + __uint_as_float(__float_as_uint(y[j]) ^ flip);
   }
 }
