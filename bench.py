@@ -76,8 +76,10 @@ def read_traffic():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the GPU needs ~30 ms of back-to-back work after idling to reach its
+    # steady clocks; 1500 headline steps are ~50 ms
+    ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--buffers", type=int, default=6, help="rotated buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
@@ -138,10 +140,25 @@ def main():
             if rc != 0:
                 raise RuntimeError(mxq.status_str(rc))
 
+    def warm(calls, seconds=0.06):
+        """Back-to-back calls for about `seconds` of GPU time (clock ramp)."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(calls, 10)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per = max(e0.elapsed_time(e1) * 1e-3 / 10, 1e-6)
+        run(calls, int(seconds / per) + 1)
+
     def time_region(calls, steps, warmup):
         """Wall time and GPU time (one event pair on the launch stream) of
-        `steps` back-to-back calls, synchronised on both sides."""
-        run(calls, warmup)
+        `steps` back-to-back calls, synchronised on both sides.  warmup=None
+        warms up for a fixed GPU time instead of a fixed count."""
+        if warmup is None:
+            warm(calls)
+        else:
+            run(calls, warmup)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -210,7 +227,7 @@ def main():
                  s["codes"].data_ptr(), s["scales"].data_ptr(), s["rrms"].data_ptr(), sp)
             tp_calls.append(lambda a=a: L.rmsnorm_mxquant_fwd(*a))
         n2 = max(30, args.steps // 4)
-        wall2, gpu2 = time_region(tp_calls, n2, 10)
+        wall2, gpu2 = time_region(tp_calls, n2, None)
         extras["two_pass_us_per_call"] = round(gpu2 / n2 * 1e6, 3)
         extras["speedup_vs_two_pass"] = round((gpu2 / n2) / kern_s, 3)
         extras["two_pass_algorithmic_GBps"] = round(two_pass_bytes(rows, hidden, w.elem)
@@ -221,7 +238,7 @@ def main():
         cbytes = 1 << 30
         pairs = [(torch.empty(cbytes, dtype=torch.uint8, device=dev),
                   torch.empty(cbytes, dtype=torch.uint8, device=dev)) for _ in range(2)]
-        for i in range(4):
+        for i in range(40):
             pairs[i % 2][1].copy_(pairs[i % 2][0])
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -247,7 +264,7 @@ def main():
             for p in wc.ps:
                 cl = mxnorm_calls(sc, gdev, r, d, p, wc.elem, wc.had)
                 nst = max(30, args.steps // 4)
-                wl, gt = time_region(cl, nst, 5)
+                wl, gt = time_region(cl, nst, None)
                 b = algorithmic_bytes(r, d, wc.elem)
                 others["%s_p%d" % (wc.name, p)] = {
                     "kernel_us_mean": round(gt / nst * 1e6, 3),
