@@ -95,6 +95,14 @@ def generate(rows: int, hidden: int, kind: str, seed: int,
     return to_bf16_bits(x), to_bf16_bits(gamma)
 
 
+def grad_output(rows: int, hidden: int, seed: int, scale: float = 1.0):
+    """Incoming gradient for the backward: scale * N(0, 1), bf16 bits.  Drawn
+    from its own stream (seed + 7919), so it does not disturb the forward draw."""
+    rng = np.random.default_rng(seed + 7919)
+    dy = rng.standard_normal((rows, hidden), dtype=np.float32)
+    return to_bf16_bits(dy * np.float32(scale))
+
+
 def workload_inputs(cfg: int, row_subset: Optional[slice] = None):
     w = WORKLOADS[cfg]
     return generate(w.rows, w.hidden, w.kind, w.seed, row_subset)

@@ -1,4 +1,4 @@
-"""CPU oracle for the MXNorm forward path -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MXNorm forward and backward paths -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It wraps the plain C reference in ``mx_oracle.c`` with
@@ -72,6 +72,9 @@ def lib():
         L.mxo_encode_array.argtypes = [C.POINTER(C.c_double), i64, C.c_int, u8p]
         L.mxo_max_threads.restype = C.c_int
         L.mxo_max_threads.argtypes = []
+        f64p = C.POINTER(C.c_double)
+        L.mxo_mxnorm_bwd.restype = C.c_int
+        L.mxo_mxnorm_bwd.argtypes = [u16p, u16p, u16p, f32p, i64, i64, f64p, f64p]
         _lib = L
     return _lib
 
@@ -222,3 +225,21 @@ def rmsnorm_mxquant_fwd(x, gamma, eps, elem):
 
 def max_threads():
     return lib().mxo_max_threads()
+
+
+def mxnorm_bwd(x, dy, gamma, rho):
+    """Straight-through MXNorm backward (fp64, unrounded): returns (dx, dgamma);
+    dgamma is None when gamma is None."""
+    x = _bf16(x)
+    dy = _bf16(dy)
+    rows, hidden = x.shape
+    assert dy.shape == x.shape
+    g = None if gamma is None else _bf16(gamma)
+    rho = np.ascontiguousarray(rho, dtype=np.float32)
+    assert rho.shape == (rows,)
+    dx = np.zeros((rows, hidden), dtype=np.float64)
+    dgamma = None if g is None else np.zeros((hidden,), dtype=np.float64)
+    _check(lib().mxo_mxnorm_bwd(_ptr(x, C.c_uint16), _ptr(dy, C.c_uint16), _ptr(g, C.c_uint16),
+                                _ptr(rho, C.c_float), rows, hidden, _ptr(dx, C.c_double),
+                                _ptr(dgamma, C.c_double)), "mxnorm_bwd")
+    return dx, dgamma

@@ -2,7 +2,7 @@
  * mx_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, deliberately obvious CPU reference for the MXNorm forward
- * path and its companions.  Only the test suite, the smoke check and the
+ * path, its straight-through backward, and their companions.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load it; the product library never calls
  * it, and it shares no code, header, table or constant with the GPU path.
  *
@@ -478,6 +478,60 @@ int mxo_rmsnorm_mxquant_fwd(const uint16_t *x, const uint16_t *gamma, int64_t ro
             }
             quantise_block(v, MXO_BLOCK, elem, codes + r * cpr, (int)(k * MXO_BLOCK),
                            &scales[r * K + k]);
+        }
+    }
+    return MXO_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * MXNorm backward (P1 §2 "Implementacion", the gradients item: a
+ * straight-through estimator that reuses the standard RMSNorm gradient, with
+ * no extra memory beyond what RMSNorm keeps).
+ *
+ * Reading taken (the pages give no formula):
+ *   - the MX cast is passed straight through: dy is the gradient with respect
+ *     to the unquantised y = x * rho * gamma;
+ *   - rho, the forward's per-row estimate saved like RMSNorm's rstd, takes
+ *     the place of rstd in RMSNorm's gradient.  With g = dy * gamma:
+ *         dx_j     = rho * g_j - rho^3 * x_j * (1/D) * sum_k x_k g_k
+ *         dgamma_j = sum over rows of dy_j * x_j * rho
+ *     (gamma == NULL: g = dy and no dgamma).
+ * The pages fix no precision; everything is evaluated in fp64 and returned
+ * unrounded.
+ * ---------------------------------------------------------------------- */
+int mxo_mxnorm_bwd(const uint16_t *x, const uint16_t *dy, const uint16_t *gamma,
+                   const float *rho, int64_t rows, int64_t hidden, double *dx,
+                   double *dgamma)
+{
+    if (rows < 0 || hidden <= 0)
+        return MXO_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        const uint16_t *xr = x + r * hidden, *dyr = dy + r * hidden;
+        const double rh = (double)rho[r];
+        double dot = 0.0; /* sum_k x_k g_k */
+        for (int64_t k = 0; k < hidden; k++) {
+            double gk = mxo_bf16_decode(dyr[k]);
+            if (gamma)
+                gk *= mxo_bf16_decode(gamma[k]);
+            dot += mxo_bf16_decode(xr[k]) * gk;
+        }
+        const double corr = rh * rh * rh * dot / (double)hidden;
+        for (int64_t j = 0; j < hidden; j++) {
+            double gj = mxo_bf16_decode(dyr[j]);
+            if (gamma)
+                gj *= mxo_bf16_decode(gamma[j]);
+            dx[r * hidden + j] = rh * gj - corr * mxo_bf16_decode(xr[j]);
+        }
+    }
+    if (gamma && dgamma) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < hidden; j++) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < rows; r++)
+                acc += mxo_bf16_decode(dy[r * hidden + j]) * mxo_bf16_decode(x[r * hidden + j]) *
+                       (double)rho[r];
+            dgamma[j] = acc;
         }
     }
     return MXO_OK;

@@ -34,6 +34,14 @@ MUTATIONS = [
     ("rms_wrong_count", "ss / (double)hidden", "ss / (double)(hidden - 1)"),
     ("e4m3_subnormal_scale", "mag = ldexp((double)m, -9); /* m/8 * 2^(1-7) */",
      "mag = ldexp((double)m, -10);"),
+    # straight-through backward
+    ("bwd_no_correction", "dx[r * hidden + j] = rh * gj - corr * mxo_bf16_decode(xr[j]);",
+     "dx[r * hidden + j] = rh * gj;"),
+    ("bwd_correction_sign", "dx[r * hidden + j] = rh * gj - corr", "dx[r * hidden + j] = rh * gj + corr"),
+    ("bwd_rho_squared", "const double corr = rh * rh * rh * dot", "const double corr = rh * rh * dot"),
+    ("bwd_divide_by_blocks", "dot / (double)hidden;", "dot / (double)(hidden / 32);"),
+    ("bwd_dot_without_gamma", "gk *= mxo_bf16_decode(gamma[k]);", "(void)gk;"),
+    ("bwd_dgamma_without_rho", "*\n                       (double)rho[r];", ";"),
 ]
 
 
@@ -49,7 +57,8 @@ def _run_mutant(name, old, new, tmp):
                     "-fopenmp", "-o", so_path, c_path, "-lm"], check=True)
     env = dict(os.environ, MXO_LIB=so_path, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_formats.py", "tests/test_oracle_mxnorm.py"],
+                        "tests/test_oracle_formats.py", "tests/test_oracle_mxnorm.py",
+                        "tests/test_oracle_bwd.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode
 
