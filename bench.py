@@ -11,7 +11,8 @@ the current stream; one HIP event pair brackets the K timed steps.
 Printed: one JSON line with the achieved algorithmic HBM throughput (GB/s),
 a roofline object for the kernel, the CPU oracle timed on the host as a
 reference baseline, and context figures (the two-pass RMSNorm + MX cast
-baseline, the other workloads, a rotated 1 GiB device copy).
+baseline, the straight-through backward on the same matrix, the other
+workloads, a rotated 1 GiB device copy).
 
 `python bench.py --counters` only runs the headline kernel and a 256 MiB
 device copy (the calibration for HBM byte counters) for rocprofv3 --pmc.
@@ -31,7 +32,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 HEADLINE = 3                     # workload number of the headline line
 METRIC = "MXNorm fwd HBM GB/s (% of MI355X peak), hidden=4096, 16k rows bf16"
 KERNEL_SOURCES = ["mx_quantised_tensor_amd/csrc/mxnorm_kernels.hip",
-                  "mx_quantised_tensor_amd/csrc/mx_device.h"]
+                  "mx_quantised_tensor_amd/csrc/mx_device.h"]  # the headline kernel's sources
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mxnorm_fwd_16384x4096_e4m3_pmc.txt")
 C_P2 = float.fromhex("0x1.c1ed54p+0")  # the library's default c(2, 32)
 
@@ -50,6 +51,13 @@ def two_pass_bytes(rows, hidden, elem):
     code_bytes = rows * hidden if elem == 0 else rows * hidden // 2
     return (2 * rows * hidden + 2 * hidden + 2 * rows * hidden + 4 * rows
             + 2 * rows * hidden + code_bytes + rows * (hidden // 32))
+
+
+def bwd_bytes(rows, hidden, gain=True):
+    """Straight-through backward: read x, dy (2 B/elem each) and rho (4 B per
+    row), write dx (2 B/elem); with the gain also read gamma and write dgamma
+    (fp32).  The dgamma partial rows (workspace) are not counted."""
+    return 6 * rows * hidden + 4 * rows + ((2 + 4) * hidden if gain else 0)
 
 
 def kernel_hash():
@@ -233,6 +241,36 @@ def main():
         extras["two_pass_algorithmic_GBps"] = round(two_pass_bytes(rows, hidden, w.elem)
                                                     / (gpu2 / n2) / 1e9, 1)
         del sets2, tp_calls
+        # straight-through backward on the same matrix (dy seeded, rho from the
+        # forward): with the gain (dx + dgamma, two launches) and without it
+        dyb = W.grad_output(rows, hidden, HEADLINE)
+        gb_dev = torch.from_numpy(gb.view(np.int16)).to(dev)
+        bsets = []
+        for i in range(3):
+            x = torch.from_numpy(xb.view(np.int16)).to(dev)
+            rr = torch.empty((rows,), dtype=torch.float32, device=dev)
+            mxq.mxnorm_fwd(x.view(torch.bfloat16), gb_dev.view(torch.bfloat16), p=2, rrms=rr)
+            bsets.append(dict(x=x, dy=torch.from_numpy(dyb.view(np.int16)).to(dev), r=rr,
+                              dx=torch.empty_like(x),
+                              dg=torch.empty((hidden,), dtype=torch.float32, device=dev),
+                              ws=torch.empty((mxq.mxnorm_bwd_workspace_bytes(rows, hidden) // 4,),
+                                             dtype=torch.float32, device=dev)))
+        for gain in (True, False):
+            bc = [lambda s=s: L.mxnorm_bwd(s["x"].data_ptr(), s["dy"].data_ptr(),
+                                            gb_dev.data_ptr() if gain else None,
+                                            s["r"].data_ptr(), rows, hidden, s["dx"].data_ptr(),
+                                            s["dg"].data_ptr() if gain else None,
+                                            s["ws"].data_ptr() if gain else None, sp)
+                  for s in bsets]
+            nb = max(30, args.steps // 4)
+            _, gt = time_region(bc, nb, None)
+            bb = bwd_bytes(rows, hidden, gain)
+            key = "mxnorm_bwd" if gain else "mxnorm_bwd_no_gain"
+            extras[key + "_us_per_call"] = round(gt / nb * 1e6, 3)
+            extras[key + "_algorithmic_GBps"] = round(bb / (gt / nb) / 1e9, 1)
+        del bsets
+        torch.cuda.empty_cache()
+
         # Context: a plain device-to-device copy (torch's copy kernel) of 1 GiB,
         # two buffer pairs rotated so the Infinity Cache cannot serve it.
         cbytes = 1 << 30

@@ -42,6 +42,7 @@
 #ifndef MXNORM_H
 #define MXNORM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -134,6 +135,41 @@ mxq_status rmsnorm_mxquant_fwd(const void *x, const void *gamma, int64_t rows,
                                int64_t hidden, float eps, mxq_elem elem,
                                void *y_workspace, uint8_t *codes, uint8_t *scales,
                                float *rstd, mxq_stream_t stream);
+
+/*
+ * mxnorm_bwd -- straight-through MXNorm backward ([P1] §2 "Implementacion",
+ * the gradients item: RMSNorm's gradient logic reused, nothing stored beyond
+ * what RMSNorm keeps).  Reading: the MX cast passes the gradient straight
+ * through (dy is taken as the gradient of the unquantised y = x*rho*gamma)
+ * and the forward's rho takes the place of RMSNorm's rstd.  With
+ * g = dy * gamma (g = dy without a gain), per row:
+ *     dx_j     = rho * g_j - rho^3 * x_j * (1/hidden) * sum_k x_k g_k
+ *     dgamma_j = sum over rows of dy_j * x_j * rho
+ * computed in fp32 (sum_k x_k g_k: per-lane FMA chains, then a fixed tree)
+ * and dx rounded to bf16 (nearest even).  dgamma is summed in an order that
+ * depends only on (rows, hidden): results are bit-reproducible run to run.
+ *   x, dy     : device bf16 [rows, hidden] (the forward's input and the
+ *               gradient of its output), 16-byte aligned
+ *   gamma     : device bf16 [hidden], 16-byte aligned, or NULL
+ *   rrms      : device fp32 [rows], rho as written by mxnorm_fwd
+ *   dx        : device bf16 [rows, hidden] out, 16-byte aligned
+ *   dgamma    : device fp32 [hidden] out; required iff gamma != NULL (rows
+ *               == 0 writes zeros); ignored without a gain
+ *   workspace : device scratch of mxnorm_bwd_workspace_bytes(rows, hidden)
+ *               bytes, 16-byte aligned, caller-owned; required iff gamma !=
+ *               NULL and rows > 0; its contents on entry do not matter
+ * hidden must be a multiple of 32 and at most 4096 (MXQ_EUNSUPPORTED above).
+ * Two launches with a gain (rows, then the dgamma column sums), one without.
+ */
+mxq_status mxnorm_bwd(const void *x, const void *dy, const void *gamma, const float *rrms,
+                      int64_t rows, int64_t hidden, void *dx, float *dgamma,
+                      float *workspace, mxq_stream_t stream);
+
+/*
+ * mxnorm_bwd_workspace_bytes -- host function: bytes of the workspace
+ * mxnorm_bwd needs with a gain (0 for rows == 0 or unsupported shapes).
+ */
+size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 
 /*
  * mxnorm_default_c -- host function.  Default c(p, 32) for power-of-two block

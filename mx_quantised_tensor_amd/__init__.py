@@ -16,6 +16,7 @@ import os
 import torch
 
 __all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
+           "mxnorm_bwd", "mxnorm_bwd_workspace_bytes",
            "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
            "library_path"]
 
@@ -57,6 +58,10 @@ def lib():
         L.mxnorm_hadamard_fwd.argtypes = [vp, vp, i64, i64, i32, f32, i32, i32, vp, vp, vp, vp]
         L.rmsnorm_mxquant_fwd.restype = i32
         L.rmsnorm_mxquant_fwd.argtypes = [vp, vp, i64, i64, f32, i32, vp, vp, vp, vp, vp]
+        L.mxnorm_bwd.restype = i32
+        L.mxnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
+        L.mxnorm_bwd_workspace_bytes.restype = C.c_size_t
+        L.mxnorm_bwd_workspace_bytes.argtypes = [i64, i64]
         L.mxnorm_default_c.restype = f32
         L.mxnorm_default_c.argtypes = [i32]
         L.mxq_status_str.restype = C.c_char_p
@@ -176,3 +181,36 @@ def rmsnorm_mxquant_fwd(x, gamma=None, eps=1e-5, elem=E4M3, y=None, codes=None, 
                                      _ptr(codes), _ptr(scales), _ptr(rstd), _stream(stream)),
            "rmsnorm_mxquant_fwd")
     return y, codes, scales, rstd
+
+
+def mxnorm_bwd_workspace_bytes(rows: int, hidden: int) -> int:
+    return int(lib().mxnorm_bwd_workspace_bytes(rows, hidden))
+
+
+def mxnorm_bwd(x, dy, rrms, gamma=None, dx=None, dgamma=None, workspace=None, stream=None):
+    """Straight-through MXNorm backward -> (dx bf16, dgamma fp32 or None).
+
+    x, dy: bf16 [rows, hidden]; rrms: fp32 [rows] from the forward.  The
+    workspace (needed with a gain) is allocated here unless one is passed."""
+    x = _bf16_2d(x)
+    dy = _bf16_2d(dy)
+    rows, hidden = x.shape
+    if tuple(dy.shape) != (rows, hidden):
+        raise ValueError("dy must have the shape of x")
+    if rrms.dtype != torch.float32 or rrms.numel() != rows or not rrms.is_cuda:
+        raise ValueError("rrms must be a device fp32 tensor with one value per row")
+    gamma = _gamma(gamma, hidden)
+    if dx is None:
+        dx = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device)
+    if gamma is not None:
+        if dgamma is None:
+            dgamma = torch.empty((hidden,), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            nbytes = mxnorm_bwd_workspace_bytes(rows, hidden)
+            workspace = torch.empty((max(nbytes, 16) // 4,), dtype=torch.float32,
+                                    device=x.device)
+    else:
+        dgamma = None
+    _check(lib().mxnorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(rrms), rows, hidden, _ptr(dx),
+                            _ptr(dgamma), _ptr(workspace), _stream(stream)), "mxnorm_bwd")
+    return dx, dgamma

@@ -28,4 +28,26 @@ hipError_t launch_mx_quant(const void* x, int64_t rows, int hidden, int elem, ui
 hipError_t launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int hidden, float eps,
                           void* y, float* rstd, void* stream);
 
+// Straight-through MXNorm backward.  hidden <= kBwdMaxHidden.
+constexpr int kBwdMaxHidden = 4096;
+// Persistent workgroups of the backward with a gain (4 waves each); tuned on
+// MI355X, where fewer rows in flight stream faster for this kernel.
+constexpr int64_t kBwdMaxGroups = 192;
+
+struct BwdLaunch {
+  const void* x;
+  const void* dy;
+  const void* gamma;  // nullptr: no gain, no dgamma
+  const float* rrms;
+  int64_t rows;
+  int hidden;
+  void* dx;
+  float* dgamma;     // required iff gamma
+  float* workspace;  // bwd_groups(rows, hidden) * hidden floats, required iff gamma
+  void* stream;
+};
+
+int64_t bwd_groups(int64_t rows, int hidden);
+hipError_t launch_mxnorm_bwd(const BwdLaunch& l);
+
 }  // namespace mxq

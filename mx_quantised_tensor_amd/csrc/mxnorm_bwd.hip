@@ -1,0 +1,332 @@
+// mxnorm_bwd.hip -- gfx950 kernels of the straight-through MXNorm backward.
+//
+// Source: "MXNorm: Reusing MXFP block scales for efficient tensor
+// normalisation" (gist.science summary), "Resumen tecnico" §2, the gradients
+// item of "Implementacion": a straight-through estimator reusing RMSNorm's
+// gradient, with no memory beyond what RMSNorm keeps.  Reading: the MX cast
+// is passed straight through and the forward's rho stands in for rstd, so
+// with g = dy * gamma
+//     dx_j     = rho * g_j - rho^3 * x_j * (1/D) sum_k x_k g_k
+//     dgamma_j = sum over rows of dy_j * x_j * rho.
+//
+// Like the forward, this is an HBM-bound streaming pass (read x and dy, write
+// dx: 6 bytes per element); no dense contraction, no MFMA.
+//   * one wavefront owns a row at a time (hidden <= 4096) with the same lane
+//     layout as the forward: lane `lane` holds chunk s*64 + lane at step s;
+//   * with a gain, waves are persistent over rows (row += total waves) so that
+//     each lane accumulates its columns' dgamma in registers across many
+//     rows, and each wave keeps the next row's loads in flight while it works
+//     on the current one.  Only 192 workgroups of 4 waves run (768 waves,
+//     ~1500 rows in flight): measured on MI355X, more concurrent waves make
+//     this pattern slower (8 waves per CU: +18%; 3 waves per SIMD: +14%),
+//     and 128 workgroups are too few.  At the end the 4 waves of a workgroup
+//     add their accumulators through LDS in a fixed order and the workgroup
+//     writes one partial row; a second kernel adds the partial rows column
+//     by column in a fixed order.  Both orders depend only on (rows, hidden),
+//     so results are run-to-run reproducible;
+//   * without a gain every wave takes one row (four per workgroup), as in the
+//     forward.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "mx_device.h"
+
+namespace mxq {
+
+namespace {
+
+constexpr int kBwdThreads = 256;  // 4 waves per workgroup without a gain
+constexpr int kColsumThreads = 256;
+constexpr int kColsumCols = 16;    // columns per workgroup of the partial-row sum
+constexpr int kColsumSlices = 64;  // partial rows b = slice + 64 k per thread
+constexpr int kColsumLoads = (int)((kBwdMaxGroups + kColsumSlices - 1) / kColsumSlices);
+
+constexpr int kBwdWaves = 4;  // waves per workgroup of the persistent (gain) kernel
+
+typedef unsigned int u32x4b_t __attribute__((ext_vector_type(4)));
+typedef float f32x2b_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2b_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const u32x4b_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4b_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_nt16(uint8_t* p, uint32_t a, uint32_t b, uint32_t c,
+                                           uint32_t d) {
+  const u32x4b_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4b_t*>(p));
+}
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2b_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2b_t));
+}
+
+struct BwdArgs {
+  const uint8_t* x;
+  const uint8_t* dy;
+  const uint8_t* gamma;  // nullptr: no gain, no dgamma
+  const float* rrms;
+  int64_t rows;
+  int hidden;
+  float inv_d;  // fl(1/hidden)
+  uint8_t* dx;
+  float* partial;  // [gridDim.x, hidden] when gamma != nullptr
+};
+
+template <int STEPS>
+__device__ __forceinline__ void load_row(const BwdArgs& a, int64_t row, const uint32_t (&choff)[STEPS],
+                                         uint4 (&xv)[STEPS], uint4 (&dv)[STEPS]) {
+  const int64_t base = row * (int64_t)a.hidden * 2;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) xv[s] = load_nt16(a.x + base + choff[s]);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) dv[s] = load_nt16(a.dy + base + choff[s]);
+}
+
+// dx of one row (and its dgamma contribution added to acc).
+template <bool GAMMA, int STEPS>
+__device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
+                                        const uint32_t (&choff)[STEPS], const bool (&act)[STEPS],
+                                        const uint4* s_gamma, uint4 (&xv)[STEPS],
+                                        uint4 (&dv)[STEPS], float (&acc)[GAMMA ? STEPS : 1][8]) {
+  // rho through the constant address space: a scalar load, so waiting for it
+  // never waits for vector loads issued after this row's
+  const float rho = ((const __attribute__((address_space(4))) float*)a.rrms)[row];
+
+  // s = sum_k x_k g_k (fp32; per-lane FMA chain, then a fixed wave tree)
+  float dot = 0.0f;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    if (!act[s]) continue;
+    float xf[8], g[8];
+    widen8(xv[s], xf);
+    widen8(dv[s], g);
+    if constexpr (GAMMA) {
+      float gf[8];
+      widen8(s_gamma[s * kWave + lane], gf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = g[i] * gf[i];  // exact: 8-bit x 8-bit significands
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(xf[i], g[i], dot);
+  }
+  dot = wave_sum_f32(dot);
+  // Keep only the packed row across the reduction: the barrier stops the
+  // compiler from holding the widened products of the first pass (64 more
+  // VGPRs); the second pass widens again.
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+    __asm__ volatile("" : "+v"(xv[s].x), "+v"(xv[s].y), "+v"(xv[s].z), "+v"(xv[s].w),
+                     "+v"(dv[s].x), "+v"(dv[s].y), "+v"(dv[s].z), "+v"(dv[s].w));
+  const float corr = ((rho * rho) * rho) * (dot * a.inv_d);
+
+  uint8_t* drow = a.dx + row * (int64_t)a.hidden * 2;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    if (!act[s]) continue;
+    float xf[8], dyf[8], d[8];
+    widen8(xv[s], xf);
+    widen8(dv[s], dyf);
+    float gf[8];
+    if constexpr (GAMMA) {
+      widen8(s_gamma[s * kWave + lane], gf);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float g = GAMMA ? dyf[i] * gf[i] : dyf[i];
+      d[i] = __builtin_fmaf(-corr, xf[i], rho * g);
+      if constexpr (GAMMA) acc[s][i] = __builtin_fmaf(dyf[i] * xf[i], rho, acc[s][i]);
+    }
+    store_nt16(drow + choff[s], bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]),
+               bf16x2_rne(d[4], d[5]), bf16x2_rne(d[6], d[7]));
+  }
+}
+
+template <bool GAMMA, int STEPS, bool FULL>
+__global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm_bwd(
+    const BwdArgs a) {
+  constexpr int NW = GAMMA ? kBwdWaves : 4;  // waves per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunk = a.hidden >> 3;
+  uint32_t choff[STEPS];
+  bool act[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int ch = s * kWave + lane;
+    act[s] = FULL || ch < nchunk;
+    choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;
+  }
+
+  // the gain is read once per workgroup into LDS (the kernel is persistent)
+  __shared__ uint4 s_gamma[GAMMA ? STEPS * kWave : 1];
+  if constexpr (GAMMA) {
+    for (int c = threadIdx.x; c < STEPS * kWave; c += NW * kWave)
+      s_gamma[c] = *reinterpret_cast<const uint4*>(a.gamma + (uint32_t)min(c, nchunk - 1) * 16u);
+    __syncthreads();
+  }
+
+  float acc[GAMMA ? STEPS : 1][8];
+#pragma unroll
+  for (int s = 0; s < (GAMMA ? STEPS : 1); ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[s][i] = 0.0f;
+
+  const int64_t stride = (int64_t)gridDim.x * NW;
+  int64_t row = (int64_t)blockIdx.x * NW + wave;
+  if constexpr (GAMMA) {
+    // Persistent waves keep the next row in flight while they work on this
+    // one, alternating between two register sets (no copies, so nothing
+    // waits for the next row before its turn).  The next row's loads are
+    // issued before this row's stores, so waiting for them never waits for
+    // those stores.  Past the last row the current row is loaded again
+    // (harmless, unused).
+    uint4 xa[STEPS], da[STEPS], xb[STEPS], db[STEPS];
+    if (row < a.rows) load_row<STEPS>(a, row, choff, xa, da);
+    while (row < a.rows) {
+      const int64_t r1 = row + stride;
+      load_row<STEPS>(a, r1 < a.rows ? r1 : row, choff, xb, db);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xa, da, acc);
+      row = r1;
+      if (row >= a.rows) break;
+      const int64_t r2 = row + stride;
+      load_row<STEPS>(a, r2 < a.rows ? r2 : row, choff, xa, da);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xb, db, acc);
+      row = r2;
+    }
+  } else {
+    if (row < a.rows) {  // one row per wave, as in the forward
+      uint4 xv[STEPS], dv[STEPS];
+      load_row<STEPS>(a, row, choff, xv, dv);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xv, dv, acc);
+    }
+  }
+
+  if constexpr (GAMMA) {
+    // workgroup partial of dgamma: (((w0 + w1) + w2) + ...), one step at a time
+    __shared__ float4 s_red[NW][kWave * 2];
+    float* prow = a.partial + (int64_t)blockIdx.x * a.hidden;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      s_red[wave][lane * 2] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+      s_red[wave][lane * 2 + 1] = make_float4(acc[s][4], acc[s][5], acc[s][6], acc[s][7]);
+      __syncthreads();
+      if (wave == 0 && act[s]) {
+        float4 lo = s_red[0][lane * 2], hi = s_red[0][lane * 2 + 1];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          const float4 l2 = s_red[w][lane * 2], h2 = s_red[w][lane * 2 + 1];
+          lo.x += l2.x; lo.y += l2.y; lo.z += l2.z; lo.w += l2.w;
+          hi.x += h2.x; hi.y += h2.y; hi.z += h2.z; hi.w += h2.w;
+        }
+        float4* dst = reinterpret_cast<float4*>(prow + (s * kWave + lane) * 8);
+        dst[0] = lo;
+        dst[1] = hi;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// dgamma_j = sum over the G <= kBwdMaxGroups partial rows, in a fixed order.
+// Thread (slice, q) of a workgroup loads the float4 of columns 4q..4q+3 of
+// partial rows slice, slice + 64, ... (all loads issued before the adds) and
+// adds them in that order; the 64 slice sums of a column are then added in
+// four runs of 16 consecutive slices, and the four run sums in order.
+__global__ __launch_bounds__(kColsumThreads) void k_colsum(const float* __restrict__ partial,
+                                                           int G, int hidden,
+                                                           float* __restrict__ out) {
+  __shared__ float s_part[kColsumSlices][kColsumCols];
+  __shared__ float s_run[4][kColsumCols];
+  const int q = threadIdx.x & 3;
+  const int slice = threadIdx.x >> 2;
+  const int col0 = blockIdx.x * kColsumCols + q * 4;  // hidden % 16 == 0: in range
+  float4 v[kColsumLoads];
+#pragma unroll
+  for (int k = 0; k < kColsumLoads; ++k) {
+    const int b = slice + k * kColsumSlices;
+    v[k] = b < G ? *reinterpret_cast<const float4*>(partial + (int64_t)b * hidden + col0)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 acc = v[0];
+#pragma unroll
+  for (int k = 1; k < kColsumLoads; ++k) {
+    acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+  }
+  s_part[slice][q * 4 + 0] = acc.x;
+  s_part[slice][q * 4 + 1] = acc.y;
+  s_part[slice][q * 4 + 2] = acc.z;
+  s_part[slice][q * 4 + 3] = acc.w;
+  __syncthreads();
+  if (threadIdx.x < 4 * kColsumCols) {
+    const int c = threadIdx.x % kColsumCols, run = threadIdx.x / kColsumCols;
+    float t = s_part[run * 16][c];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) t += s_part[run * 16 + i][c];
+    s_run[run][c] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < kColsumCols) {
+    const int c = threadIdx.x;
+    out[blockIdx.x * kColsumCols + c] = ((s_run[0][c] + s_run[1][c]) + s_run[2][c]) + s_run[3][c];
+  }
+}
+
+template <bool GAMMA, int STEPS>
+hipError_t launch_bwd_t(const BwdArgs& a, int groups, void* stream) {
+  const dim3 block(GAMMA ? kBwdWaves * 64 : kBwdThreads);
+  if (a.hidden == 512 * STEPS)
+    hipLaunchKernelGGL((k_mxnorm_bwd<GAMMA, STEPS, true>), dim3(groups), block, 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((k_mxnorm_bwd<GAMMA, STEPS, false>), dim3(groups), block, 0,
+                       (hipStream_t)stream, a);
+  return hipGetLastError();
+}
+
+template <bool GAMMA>
+hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
+  const int nchunk = a.hidden / 8;
+  if (nchunk <= 64) return launch_bwd_t<GAMMA, 1>(a, groups, stream);
+  if (nchunk <= 128) return launch_bwd_t<GAMMA, 2>(a, groups, stream);
+  if (nchunk <= 256) return launch_bwd_t<GAMMA, 4>(a, groups, stream);
+  return launch_bwd_t<GAMMA, 8>(a, groups, stream);
+}
+
+}  // namespace
+
+int64_t bwd_groups(int64_t rows, int hidden) {
+  (void)hidden;
+  const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
+  return need < kBwdMaxGroups ? need : kBwdMaxGroups;
+}
+
+hipError_t launch_mxnorm_bwd(const BwdLaunch& l) {
+  BwdArgs a;
+  a.x = static_cast<const uint8_t*>(l.x);
+  a.dy = static_cast<const uint8_t*>(l.dy);
+  a.gamma = static_cast<const uint8_t*>(l.gamma);
+  a.rrms = l.rrms;
+  a.rows = l.rows;
+  a.hidden = l.hidden;
+  a.inv_d = 1.0f / (float)l.hidden;
+  a.dx = static_cast<uint8_t*>(l.dx);
+  a.partial = l.workspace;
+  // with a gain the workgroups are persistent (one dgamma partial row each);
+  // without one every wave takes a single row, as in the forward
+  const int groups = (int)(l.gamma ? bwd_groups(l.rows, l.hidden) : (l.rows + 3) / 4);
+  if (groups > 0) {
+    const hipError_t e = l.gamma ? launch_bwd_steps<true>(a, groups, l.stream)
+                                 : launch_bwd_steps<false>(a, groups, l.stream);
+    if (e != hipSuccess) return e;
+  }
+  if (l.gamma == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(k_colsum, dim3((unsigned)(l.hidden / kColsumCols)), dim3(kColsumThreads), 0,
+                     (hipStream_t)l.stream, l.workspace, groups, l.hidden, l.dgamma);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -3,6 +3,7 @@
 // host before anything is enqueued; the library never allocates, frees or
 // synchronises.
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -18,8 +19,10 @@ namespace {
 constexpr float kDefaultC1 = 0x1.b16c5ep+0f;  // 1.6930598
 constexpr float kDefaultC2 = 0x1.c1ed54p+0f;  // 1.7575276
 
-// Largest element count per call: keeps every grid dimension below 2^32.
-constexpr int64_t kMaxElems = (int64_t)1 << 40;
+// Limits per call that keep every launch below 2^32 threads (a workgroup of
+// 256 threads per row at most; one thread per 8 elements at most).
+constexpr int64_t kMaxRows = ((int64_t)1 << 24) - 1;
+constexpr int64_t kMaxElems = (int64_t)1 << 34;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -28,7 +31,7 @@ mxq_status check_shape(int64_t rows, int64_t hidden, mxq_elem elem) {
   if (elem != MXQ_E4M3 && elem != MXQ_E2M1) return MXQ_EINVAL;
   if (hidden > MXQ_MAX_HIDDEN || !mxq::row_shape_supported((int)hidden))
     return MXQ_EUNSUPPORTED;
-  if (rows > kMaxElems / hidden) return MXQ_EUNSUPPORTED;
+  if (rows > kMaxRows || rows > kMaxElems / hidden) return MXQ_EUNSUPPORTED;
   return MXQ_OK;
 }
 
@@ -116,6 +119,45 @@ mxq_status rmsnorm_mxquant_fwd(const void* x, const void* gamma, int64_t rows, i
   if (e != hipSuccess) return MXQ_EHIP;
   return status_of(
       mxq::launch_mx_quant(y_workspace, rows, (int)hidden, (int)elem, codes, scales, stream));
+}
+
+size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
+  if (rows < 0 || hidden <= 0 || hidden % MXQ_BLOCK != 0 || hidden > mxq::kBwdMaxHidden ||
+      rows > kMaxRows)
+    return 0;
+  return (size_t)mxq::bwd_groups(rows, (int)hidden) * (size_t)hidden * sizeof(float);
+}
+
+mxq_status mxnorm_bwd(const void* x, const void* dy, const void* gamma, const float* rrms,
+                      int64_t rows, int64_t hidden, void* dx, float* dgamma, float* workspace,
+                      mxq_stream_t stream) {
+  if (rows < 0 || hidden <= 0 || hidden % MXQ_BLOCK != 0) return MXQ_EINVAL;
+  if (hidden > mxq::kBwdMaxHidden || rows > kMaxRows || rows > kMaxElems / hidden)
+    return MXQ_EUNSUPPORTED;
+  if (gamma != nullptr) {
+    if (dgamma == nullptr || (rows > 0 && workspace == nullptr)) return MXQ_EINVAL;
+    if (!aligned(gamma, 16) || !aligned(dgamma, 4) || !aligned(workspace, 16)) return MXQ_EALIGN;
+  }
+  if (rows > 0) {
+    if (x == nullptr || dy == nullptr || rrms == nullptr || dx == nullptr) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(rrms, 4))
+      return MXQ_EALIGN;
+  } else if (gamma == nullptr) {
+    return MXQ_OK;  // nothing to do
+  }
+  mxq::BwdLaunch l;
+  l.x = x;
+  l.dy = dy;
+  l.gamma = gamma;
+  l.rrms = rrms;
+  l.rows = rows;
+  l.hidden = (int)hidden;
+  l.dx = dx;
+  l.dgamma = dgamma;
+  l.workspace = workspace;
+  l.stream = stream;
+  (void)hipGetLastError();
+  return status_of(mxq::launch_mxnorm_bwd(l));
 }
 
 float mxnorm_default_c(int p) {

@@ -69,3 +69,49 @@ def assert_rho_equal(got, want, what=""):
     assert bad == 0, "%s: %d of %d rho values differ (max rel %.3g)" % (
         what, bad, want.size,
         np.max(np.abs(got[~nan_w].astype(np.float64) / want[~nan_w] - 1)) if bad else 0)
+
+
+# ------------------------------------------------------------ straight-through backward
+# dx is computed in fp32 and rounded to bf16; the oracle is fp64.  With
+# u = 2^-24 and T_j = rho |g_j| + rho^3 |x_j| sum_k |x_k g_k| / D (the sizes of
+# the two terms), the fp32 evaluation is within about 80 u T_j of the exact
+# value (the dot product's FMA chain and tree, five roundings of the
+# correction, the product and the final FMA); rounding to bf16 adds half a
+# bf16 ulp.  The bar allows one bf16 ulp of the exact value plus 2^-16 T_j.
+# dgamma sums fp32 contributions over rows in chains of at most a few hundred
+# additions for the sizes tested: the bar is 2^-12 of sum |dy x rho|.
+
+def bf16_bits_to_f64(bits):
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(a > 0, np.exp2(e - 7), 2.0 ** -133)
+
+
+def assert_bwd_close(dx_bits, dgamma, x_bits, dy_bits, g_bits, rho, ref_dx, ref_dg, what=""):
+    x = bf16_bits_to_f64(x_bits)
+    gv = bf16_bits_to_f64(dy_bits)
+    if g_bits is not None:
+        gv = gv * bf16_bits_to_f64(g_bits)[None, :]
+    r = rho.astype(np.float64)[:, None]
+    d = x.shape[1]
+    T = r * np.abs(gv) + r ** 3 * np.abs(x) * np.sum(np.abs(x * gv), axis=1, keepdims=True) / d
+    got = bf16_bits_to_f64(dx_bits)
+    finite = np.isfinite(ref_dx)
+    err = np.abs(got - ref_dx)
+    bound = bf16_ulp(ref_dx) + 2.0 ** -16 * T
+    bad = finite & ~(err <= bound)
+    assert not bad.any(), "%s: dx off at %d elements, worst %r (bound %r)" % (
+        what, int(bad.sum()), float(err[bad].max()), float(bound[bad][np.argmax(err[bad])]))
+    assert np.array_equal(np.isnan(got), np.isnan(ref_dx)), what + ": NaN pattern of dx"
+    if ref_dg is not None:
+        scale = np.sum(np.abs(bf16_bits_to_f64(dy_bits) * x * r), axis=0)
+        e = np.abs(dgamma.astype(np.float64) - ref_dg)
+        ok = e <= 2.0 ** -12 * scale + 1e-30
+        assert ok.all(), "%s: dgamma off at %d columns, worst rel %r" % (
+            what, int((~ok).sum()), float(np.max(e / np.maximum(scale, 1e-300))))

@@ -30,7 +30,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     L = mxq.lib()
     names = declared_functions()
     assert set(names) >= {"mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd",
-                          "rmsnorm_mxquant_fwd", "mxnorm_default_c", "mxq_status_str"}
+                          "rmsnorm_mxquant_fwd", "mxnorm_bwd", "mxnorm_bwd_workspace_bytes",
+                          "mxnorm_default_c", "mxq_status_str"}
     for n in names:
         assert hasattr(L, n), n
     assert mxq.lib().mxq_version().decode().startswith("mxnorm-gfx950")
@@ -78,9 +79,46 @@ def test_bad_hidden(hidden):
     assert _rms(hidden=hidden) == EINVAL
 
 
+def _bwd(x=A16, dy=A16, g=None, rrms=A16, rows=4, hidden=64, dx=A16, dg=None, ws=None):
+    return mxq.lib().mxnorm_bwd(x, dy, g, rrms, rows, hidden, dx, dg, ws, None)
+
+
 def test_hidden_above_limit_unsupported():
     assert _mxq(hidden=mxq.MAX_HIDDEN + 32) == EUNSUP
     assert _mxn(hidden=mxq.MAX_HIDDEN * 2) == EUNSUP
+    assert _bwd(hidden=4096 + 32) == EUNSUP
+
+
+def test_row_count_limit():
+    # every launch stays below 2^32 threads: at most 2^24 - 1 rows, 2^34 elements
+    assert _mxn(rows=1 << 24) == EUNSUP
+    assert _mxq(rows=(1 << 34) // 4096 + 1, hidden=4096) == EUNSUP
+    assert _bwd(rows=1 << 24) == EUNSUP
+
+
+def test_bwd_argument_checks():
+    assert _bwd(hidden=48) == EINVAL
+    assert _bwd(rows=-1) == EINVAL
+    assert _bwd(x=None) == EINVAL
+    assert _bwd(rrms=None) == EINVAL
+    assert _bwd(dx=None) == EINVAL
+    assert _bwd(g=A16) == EINVAL                 # a gain needs dgamma and a workspace
+    assert _bwd(g=A16, dg=A16) == EINVAL
+    assert _bwd(dy=MIS) == EALIGN
+    assert _bwd(dx=MIS) == EALIGN
+    assert _bwd(rrms=A16 + 2) == EALIGN
+    assert _bwd(g=MIS, dg=A16, ws=A16) == EALIGN
+    assert _bwd(g=A16, dg=A16, ws=MIS) == EALIGN
+    assert _bwd(rows=0, x=None, dy=None, rrms=None, dx=None) == OK
+
+
+def test_bwd_workspace_size():
+    ws = mxq.mxnorm_bwd_workspace_bytes
+    assert ws(0, 4096) == 0
+    assert ws(1, 64) == 64 * 4            # one workgroup
+    assert ws(5, 64) == 2 * 64 * 4        # ceil(5 / 4) workgroups of 4 waves
+    assert ws(16384, 4096) == 192 * 4096 * 4
+    assert ws(16, 8192) == 0 and ws(16, 48) == 0 and ws(-1, 64) == 0
 
 
 def test_negative_rows_and_bad_elem():

@@ -1,0 +1,119 @@
+"""GPU parity of the straight-through MXNorm backward (libmxnorm.so through
+its C ABI) against the fp64 CPU oracle on the same seeded inputs.  Run on an
+MI355X with ``pytest -m gpu``.  Bars are in tests/parity.py (dx within one
+bf16 ulp plus 2^-16 of its terms; dgamma within 2^-12 of sum |dy x rho|);
+dx and dgamma must also be bit-identical from run to run."""
+import numpy as np
+import pytest
+import torch
+
+import mx_quantised_tensor_amd as mxq
+import oracle as O
+from mx_quantised_tensor_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+C2 = float.fromhex("0x1.c1ed54p+0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    mxq.lib()
+    yield
+
+
+def _inputs(rows, hidden, kind="outlier", seed=21, with_gamma=True):
+    xb, gb = W.generate(rows, hidden, kind, seed)
+    dyb = W.grad_output(rows, hidden, seed)
+    _, _, rho = O.mxnorm_fwd(xb, gb, 2, C2, O.E4M3)
+    return xb, dyb, (gb if with_gamma else None), rho
+
+
+def _run(xb, dyb, gb, rho):
+    x, dy = P.to_device_bf16(xb), P.to_device_bf16(dyb)
+    g = None if gb is None else P.to_device_bf16(gb)
+    r = torch.from_numpy(np.ascontiguousarray(rho)).cuda()
+    dx, dg = mxq.mxnorm_bwd(x, dy, r, g)
+    torch.cuda.synchronize()
+    dxb = P.from_device(dx.view(torch.int16)).view(np.uint16)
+    return dxb, (None if dg is None else P.from_device(dg))
+
+
+def _check(xb, dyb, gb, rho, what):
+    print("case:", what, flush=True)
+    dxb, dg = _run(xb, dyb, gb, rho)
+    ref_dx, ref_dg = O.mxnorm_bwd(xb, dyb, gb, rho)
+    P.assert_bwd_close(dxb, dg, xb, dyb, gb, rho, ref_dx, ref_dg, what)
+    return dxb, dg
+
+
+@pytest.mark.parametrize("with_gamma", [True, False])
+@pytest.mark.parametrize("hidden", [32, 96, 512, 768, 1024, 1536, 2048, 4064, 4096])
+def test_bwd_shapes(hidden, with_gamma):
+    for rows in (1, 3, 5, 67):
+        xb, dyb, gb, rho = _inputs(rows, hidden, with_gamma=with_gamma, seed=hidden + rows)
+        _check(xb, dyb, gb, rho, "rows=%d hidden=%d gamma=%s" % (rows, hidden, with_gamma))
+
+
+@pytest.mark.parametrize("kind", ["outlier", "rowscale", "t3"])
+def test_bwd_many_rows_persistent(kind):
+    # more rows than the persistent grid holds waves: every wave takes several rows
+    xb, dyb, gb, rho = _inputs(6000, 1024, kind=kind, seed=31)
+    _check(xb, dyb, gb, rho, "6000x1024 " + kind)
+
+
+def test_bwd_headline_shape_and_reproducible():
+    # the 16384 x 4096 activation matrix of the headline forward; dgamma over all
+    # rows; dx compared on every row
+    xb, _ = W.workload_inputs(3)
+    gb = W.workload_inputs(3)[1]
+    dyb = W.grad_output(16384, 4096, 3)
+    x = P.to_device_bf16(xb)
+    g = P.to_device_bf16(gb)
+    _, _, rho_d = mxq.mxnorm_fwd(x, g, p=2)
+    rho = P.from_device(rho_d)
+    dxb, dg = _check(xb, dyb, gb, rho, "16384x4096 rowscale")
+    dxb2, dg2 = _run(xb, dyb, gb, rho)
+    assert np.array_equal(dxb, dxb2) and np.array_equal(dg.view(np.uint32), dg2.view(np.uint32))
+
+
+def test_bwd_zero_rows_gives_zero_dgamma():
+    g = P.to_device_bf16(W.generate(1, 256, "outlier", 1)[1])
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    r = torch.empty((0,), dtype=torch.float32, device="cuda")
+    dg = torch.full((256,), 7.0, dtype=torch.float32, device="cuda")
+    dx, dg = mxq.mxnorm_bwd(x, x, r, g, dgamma=dg)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 256) and not dg.cpu().numpy().any()
+
+
+def test_bwd_nonfinite_row_stays_local():
+    xb, dyb, gb, rho = _inputs(8, 512, seed=41)
+    xb = xb.copy()
+    xb[3, 17] = 0x7F80  # +Inf: the forward gives this row rho = NaN
+    _, _, rho = O.mxnorm_fwd(xb, gb, 2, C2, O.E4M3)
+    assert np.isnan(rho[3])
+    dxb, dg = _run(xb, dyb, gb, rho)
+    dx = P.bf16_bits_to_f64(dxb)
+    assert np.isnan(dx[3]).all()
+    keep = np.arange(8) != 3
+    ref_dx, _ = O.mxnorm_bwd(xb[keep], dyb[keep], gb, rho[keep])
+    P.assert_bwd_close(dxb[keep], None, xb[keep], dyb[keep], gb, rho[keep], ref_dx, None,
+                       "finite rows next to a NaN row")
+    assert np.isnan(dg).all()  # the NaN row enters every column's sum
+
+
+def test_bwd_on_side_stream():
+    xb, dyb, gb, rho = _inputs(300, 2048, seed=51)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x, dy = P.to_device_bf16(xb), P.to_device_bf16(dyb)
+        g = P.to_device_bf16(gb)
+        r = torch.from_numpy(rho).cuda()
+        dx, dg = mxq.mxnorm_bwd(x, dy, r, g, stream=s)
+    s.synchronize()
+    ref_dx, ref_dg = O.mxnorm_bwd(xb, dyb, gb, rho)
+    P.assert_bwd_close(P.from_device(dx.view(torch.int16)).view(np.uint16), P.from_device(dg),
+                       xb, dyb, gb, rho, ref_dx, ref_dg, "side stream")
