@@ -157,42 +157,15 @@ struct WaveArgs {
   int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
 };
 
+// The whole forward of one row held in VGPRs (v: the row, gr: the gain).
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL>
-__global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+__device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lane,
+                                         const bool (&act)[STEPS], const uint4 (&v)[STEPS],
+                                         const uint4 (&gr)[GAMMA ? STEPS : 1],
+                                         uint32_t* __restrict__ s_sc) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
-  __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= a.rows) return;  // whole wave; no barriers in this kernel
-
-  const int nchunk = a.hidden >> 3;
   const int K = a.hidden >> 5;
-  uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
-  bool act[STEPS];
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int ch = s * kWave + lane;
-    act[s] = FULL || ch < nchunk;  // uniform over each quad (nchunk % 4 == 0)
-    choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;  // clamped: stays in the row
-  }
-
-  const uint8_t* xrow = a.x + row * (int64_t)a.hidden * 2;
-  uint4 v[STEPS];
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + choff[s]);
-  // the gain (L2-resident) is requested with the row, so it has arrived by the
-  // time the row statistic is done
-  uint4 gr[GAMMA ? STEPS : 1];
-  if constexpr (GAMMA) {
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(a.gamma + choff[s]);
-  } else {
-    gr[0] = make_uint4(0, 0, 0, 0);
-  }
-
   int u[STEPS];
   int umax = kInactive;
 #pragma unroll
@@ -221,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
     if (!FULL && !act[s]) continue;  // quad-uniform; the DPP inside stays in the quad
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(
         v[s], gr[GAMMA ? s : 0], rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
-    reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
+    reinterpret_cast<uint8_t*>(s_sc)[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
   // the scale bytes written above are read back by other lanes of the wave
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -229,14 +202,52 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint8_t* srow = a.scales + row * K;
   if (a.scales_dwords) {  // K / 4 <= STEPS * 4 <= 32 dwords: one store per lane
-    if (lane < (K >> 2)) reinterpret_cast<uint32_t*>(srow)[lane] = s_sc[wave][lane];
+    if (lane < (K >> 2)) reinterpret_cast<uint32_t*>(srow)[lane] = s_sc[lane];
   } else {
 #pragma unroll
     for (int j = 0; j < (STEPS * 16 + kWave - 1) / kWave; ++j) {
       const int i = j * kWave + lane;
-      if (i < K) srow[i] = reinterpret_cast<const uint8_t*>(s_sc[wave])[i];
+      if (i < K) srow[i] = reinterpret_cast<const uint8_t*>(s_sc)[i];
     }
   }
+}
+
+template <int STEPS, bool FULL>
+__device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[STEPS],
+                                            uint32_t (&choff)[STEPS]) {
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int ch = s * kWave + lane;
+    act[s] = FULL || ch < nchunk;  // uniform over each quad (nchunk % 4 == 0)
+    choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;  // clamped: stays in the row
+  }
+}
+
+template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+  __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= a.rows) return;  // whole wave; no barriers in this kernel
+
+  uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
+  bool act[STEPS];
+  lane_chunks<STEPS, FULL>(lane, a.hidden >> 3, act, choff);
+  const uint8_t* xrow = a.x + row * (int64_t)a.hidden * 2;
+  uint4 v[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + choff[s]);
+  // the gain (L2-resident) is requested with the row, so it has arrived by the
+  // time the row statistic is done
+  uint4 gr[GAMMA ? STEPS : 1];
+  if constexpr (GAMMA) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(a.gamma + choff[s]);
+  } else {
+    gr[0] = make_uint4(0, 0, 0, 0);
+  }
+  wave_row<ELEM, GAMMA, HAD, STEPS, FULL>(a, row, lane, act, v, gr, s_sc[wave]);
 }
 
 // ----------------------------------------------------------------------------------
