@@ -17,6 +17,8 @@ from . import build as _build
 E4M3 = 0
 E2M1 = 1
 BLOCK = 32
+SRC_SCALES = 0   # block magnitude = the E8M0 scale as a power of two
+SRC_ABSMAX = 1   # block magnitude = the exact block absmax
 
 _lib = None
 
@@ -73,6 +75,14 @@ def lib():
         L.mxo_max_threads.restype = C.c_int
         L.mxo_max_threads.argtypes = []
         f64p = C.POINTER(C.c_double)
+        L.mxo_mxnorm_fwd_ex.restype = C.c_int
+        L.mxo_mxnorm_fwd_ex.argtypes = [u16p, u16p, i64, i64, C.c_int, C.c_float, C.c_int,
+                                        C.c_int, C.c_int, u8p, u8p, f32p]
+        L.mxo_row_stat_absmax.restype = C.c_int
+        L.mxo_row_stat_absmax.argtypes = [u16p, i64, C.c_int, C.POINTER(C.c_int),
+                                          C.POINTER(C.c_uint64)]
+        L.mxo_rho_absmax.restype = C.c_float
+        L.mxo_rho_absmax.argtypes = [C.c_int, C.c_uint64, i64, C.c_int, C.c_float]
         L.mxo_mxnorm_bwd.restype = C.c_int
         L.mxo_mxnorm_bwd.argtypes = [u16p, u16p, u16p, f32p, i64, i64, f64p, f64p]
         _lib = L
@@ -243,3 +253,31 @@ def mxnorm_bwd(x, dy, gamma, rho):
                                 _ptr(rho, C.c_float), rows, hidden, _ptr(dx, C.c_double),
                                 _ptr(dgamma, C.c_double)), "mxnorm_bwd")
     return dx, dgamma
+
+
+def mxnorm_fwd_ex(x, gamma, p, c, source, had, elem):
+    """Forward with either block-magnitude reading (and optional rotation)."""
+    x = _bf16(x)
+    rows, hidden = x.shape
+    g = None if gamma is None else _bf16(gamma)
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    rrms = np.zeros((rows,), dtype=np.float32)
+    _check(lib().mxo_mxnorm_fwd_ex(_ptr(x, C.c_uint16), _ptr(g, C.c_uint16), rows, hidden, p, c,
+                                   source, had, elem, _ptr(codes, C.c_uint8),
+                                   _ptr(scales, C.c_uint8), _ptr(rrms, C.c_float)),
+           "mxnorm_fwd_ex")
+    return codes, scales, rrms
+
+
+def row_stat_absmax(xrow, p):
+    xrow = _bf16(xrow)
+    E = C.c_int()
+    S = C.c_uint64()
+    _check(lib().mxo_row_stat_absmax(_ptr(xrow, C.c_uint16), xrow.size, p, C.byref(E),
+                                     C.byref(S)), "row_stat_absmax")
+    return E.value, S.value
+
+
+def rho_absmax(E, S, K, p, c):
+    return float(np.float32(lib().mxo_rho_absmax(E, S, K, p, c)))

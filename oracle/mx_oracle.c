@@ -40,6 +40,11 @@
 #define MXO_E4M3 0
 #define MXO_E2M1 1
 
+/* Which block magnitude enters the power mean (see mxo_row_stat and
+ * mxo_row_stat_absmax). */
+#define MXO_SRC_SCALES 0
+#define MXO_SRC_ABSMAX 1
+
 /* Block size of the MX formats (P2 abstract: reduction 32x smaller; P1 §3). */
 #define MXO_BLOCK 32
 
@@ -344,6 +349,97 @@ float mxo_rho(int E, uint64_t S, int64_t K, int p, float c)
     return ldexpf(q, 40 / p - E);
 }
 
+/* ------------------------------------------------------------------------
+ * The other reading of the block magnitude: P1 §2 "Formula" writes the
+ * estimate over the block absmax itself, mt_k = m_k = max_i |x_i| (exact),
+ * rather than its power-of-two E8M0 scale.
+ *
+ * Exact evaluation: a bf16 absmax has 8 significant bits, so with
+ *     E_k = max(floor(log2 m_k), -126)   (-126 for a zero block)
+ *     M_k = m_k * 2^(7 - E_k)            (an integer in [0, 255])
+ * and E = max_k E_k,
+ *     (1/K) sum m_k^p = 2^(p (E - 7) - 24) * S / K,
+ *     S = sum_k [p (E - E_k) <= 24] * M_k^p * 2^(24 - p (E - E_k)),
+ * an integer below 2^50 for K <= 1024 (terms whose exponent is more than
+ * 24 / p below the largest are dropped).  E = 1000 marks a row with NaN/Inf.
+ * ---------------------------------------------------------------------- */
+static void block_absmax_parts(double m, int *E_k, uint64_t *M_k)
+{
+    if (m == 0.0) {
+        *E_k = -126;
+        *M_k = 0;
+        return;
+    }
+    int ex;
+    (void)frexp(m, &ex); /* m = f * 2^ex, f in [0.5, 1): floor(log2 m) = ex - 1 */
+    int e = ex - 1;
+    if (e < -126)
+        e = -126;
+    *E_k = e;
+    *M_k = (uint64_t)ldexp(m, 7 - e); /* exact: 8 significant bits */
+}
+
+int mxo_row_stat_absmax(const uint16_t *xrow, int64_t hidden, int p, int *E_out,
+                        uint64_t *S_out)
+{
+    const int64_t K = hidden / MXO_BLOCK;
+    int E = -100000, nonfinite = 0;
+    for (int64_t k = 0; k < K; k++) {
+        double amax = 0.0;
+        for (int i = 0; i < MXO_BLOCK; i++) {
+            double v = mxo_bf16_decode(xrow[k * MXO_BLOCK + i]);
+            if (!isfinite(v))
+                nonfinite = 1;
+            else if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        int ek;
+        uint64_t mk;
+        block_absmax_parts(amax, &ek, &mk);
+        if (ek > E)
+            E = ek;
+    }
+    if (nonfinite) {
+        *E_out = 1000;
+        *S_out = 0;
+        return MXO_OK;
+    }
+    uint64_t S = 0;
+    for (int64_t k = 0; k < K; k++) {
+        double amax = 0.0;
+        for (int i = 0; i < MXO_BLOCK; i++) {
+            double v = fabs(mxo_bf16_decode(xrow[k * MXO_BLOCK + i]));
+            if (v > amax)
+                amax = v;
+        }
+        int ek;
+        uint64_t mk;
+        block_absmax_parts(amax, &ek, &mk);
+        int t = p * (E - ek);
+        if (t <= 24) {
+            uint64_t mp = (p == 1) ? mk : mk * mk;
+            S += mp << (24 - t);
+        }
+    }
+    *E_out = E;
+    *S_out = S;
+    return MXO_OK;
+}
+
+/* rho for the absmax reading: mu = fl(fl(S) / K); r = mu (p = 1) or
+ * fl(sqrt(mu)) (p = 2); rho = fl(c / r) * 2^(24/p + 7 - E).  An all-zero row
+ * has S = 0 and no RMS to estimate: rho = +Inf. */
+float mxo_rho_absmax(int E, uint64_t S, int64_t K, int p, float c)
+{
+    if (E == 1000)
+        return NAN;
+    float Sf = (float)S;
+    float mu = Sf / (float)K;
+    float r = (p == 1) ? mu : sqrtf(mu);
+    float q = c / r;
+    return ldexpf(q, 24 / p + 7 - E);
+}
+
 /* In-place fast Walsh-Hadamard transform of each group of `had` values
  * (had = 16 or 32), natural (Sylvester) order, in fp32, butterfly distance
  * h = 1, 2, 4, ...; each butterfly maps (a, b) -> (a + b, a - b); then the
@@ -376,9 +472,11 @@ void mxo_fwht_f32(float *y, int64_t n, int had)
  *   scales re-derived from y.  rrms (optional) receives rho per row.
  * ---------------------------------------------------------------------- */
 static int mxnorm_common(const uint16_t *x, const uint16_t *gamma, int64_t rows,
-                         int64_t hidden, int p, float c, int had, int elem,
+                         int64_t hidden, int p, float c, int source, int had, int elem,
                          uint8_t *codes, uint8_t *scales, float *rrms)
 {
+    if (source != MXO_SRC_SCALES && source != MXO_SRC_ABSMAX)
+        return MXO_EINVAL;
     if (check_shape(rows, hidden, elem) != MXO_OK)
         return MXO_EINVAL;
     if (p != 1 && p != 2)
@@ -397,8 +495,14 @@ static int mxnorm_common(const uint16_t *x, const uint16_t *gamma, int64_t rows,
         const uint16_t *xr = x + r * hidden;
         int E;
         uint64_t S;
-        mxo_row_stat(xr, hidden, p, emax, &E, &S);
-        float rho = mxo_rho(E, S, K, p, c);
+        float rho;
+        if (source == MXO_SRC_SCALES) {
+            mxo_row_stat(xr, hidden, p, emax, &E, &S);
+            rho = mxo_rho(E, S, K, p, c);
+        } else {
+            mxo_row_stat_absmax(xr, hidden, p, &E, &S);
+            rho = mxo_rho_absmax(E, S, K, p, c);
+        }
         if (rrms)
             rrms[r] = rho;
         float y[MXO_BLOCK];
@@ -423,7 +527,16 @@ static int mxnorm_common(const uint16_t *x, const uint16_t *gamma, int64_t rows,
 int mxo_mxnorm_fwd(const uint16_t *x, const uint16_t *gamma, int64_t rows, int64_t hidden,
                    int p, float c, int elem, uint8_t *codes, uint8_t *scales, float *rrms)
 {
-    return mxnorm_common(x, gamma, rows, hidden, p, c, 0, elem, codes, scales, rrms);
+    return mxnorm_common(x, gamma, rows, hidden, p, c, MXO_SRC_SCALES, 0, elem, codes, scales,
+                         rrms);
+}
+
+/* Both readings of the block magnitude and the optional rotation in one call. */
+int mxo_mxnorm_fwd_ex(const uint16_t *x, const uint16_t *gamma, int64_t rows, int64_t hidden,
+                      int p, float c, int source, int had, int elem, uint8_t *codes,
+                      uint8_t *scales, float *rrms)
+{
+    return mxnorm_common(x, gamma, rows, hidden, p, c, source, had, elem, codes, scales, rrms);
 }
 
 int mxo_mxnorm_hadamard_fwd(const uint16_t *x, const uint16_t *gamma, int64_t rows,
@@ -432,7 +545,8 @@ int mxo_mxnorm_hadamard_fwd(const uint16_t *x, const uint16_t *gamma, int64_t ro
 {
     if (had != 16 && had != 32)
         return MXO_EINVAL;
-    return mxnorm_common(x, gamma, rows, hidden, p, c, had, elem, codes, scales, rrms);
+    return mxnorm_common(x, gamma, rows, hidden, p, c, MXO_SRC_SCALES, had, elem, codes, scales,
+                         rrms);
 }
 
 /* ------------------------------------------------------------------------

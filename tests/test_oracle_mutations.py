@@ -42,6 +42,11 @@ MUTATIONS = [
     ("bwd_divide_by_blocks", "dot / (double)hidden;", "dot / (double)(hidden / 32);"),
     ("bwd_dot_without_gamma", "gk *= mxo_bf16_decode(gamma[k]);", "(void)gk;"),
     ("bwd_dgamma_without_rho", "*\n                       (double)rho[r];", ";"),
+    # exact-absmax reading of the block magnitude
+    ("absmax_drop_threshold", "if (t <= 24) {\n            uint64_t mp", "if (t <= 20) {\n            uint64_t mp"),
+    ("absmax_exponent_offset", "return ldexpf(q, 24 / p + 7 - E);", "return ldexpf(q, 24 / p - E);"),
+    ("absmax_power_ignored", "uint64_t mp = (p == 1) ? mk : mk * mk;", "uint64_t mp = mk;"),
+    ("absmax_no_subnormal_clamp", "if (e < -126)\n        e = -126;\n    *E_k = e;", "*E_k = e;"),
 ]
 
 
@@ -58,7 +63,7 @@ def _run_mutant(name, old, new, tmp):
     env = dict(os.environ, MXO_LIB=so_path, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_mxnorm.py",
-                        "tests/test_oracle_bwd.py"],
+                        "tests/test_oracle_bwd.py", "tests/test_oracle_absmax.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode
 
