@@ -65,6 +65,12 @@ typedef enum {
     MXQ_E2M1 = 1            /* MXFP4: E2M1 elements, 2 per byte */
 } mxq_elem;
 
+/* Which block magnitude enters the MXNorm power mean. */
+typedef enum {
+    MXQ_SRC_SCALES = 0,     /* 2^(e_k + emax): the E8M0 scale of block k as a power of two */
+    MXQ_SRC_ABSMAX = 1      /* the exact block absmax max_i |x_i| */
+} mxq_source;
+
 #define MXQ_BLOCK 32
 #define MXQ_MAX_HIDDEN 32768
 
@@ -118,6 +124,29 @@ mxq_status mxnorm_hadamard_fwd(const void *x, const void *gamma, int64_t rows,
                                int64_t hidden, int p, float c, int had, mxq_elem elem,
                                uint8_t *codes, uint8_t *scales, float *rrms,
                                mxq_stream_t stream);
+
+/*
+ * mxnorm_fwd_ex -- mxnorm_fwd / mxnorm_hadamard_fwd with a choice of block
+ * magnitude.  [P2]'s abstract has MXNorm use only the block scales of the
+ * cast (MXQ_SRC_SCALES, what mxnorm_fwd computes); [P1] §2 "Formula" writes
+ * the estimate over the block absmax itself (MXQ_SRC_ABSMAX):
+ *   mt_k = m_k = max_i |x_i| of block k, exactly.  With
+ *   E_k = max(floor(log2 m_k), -126) (-126 for a zero block), the 8-bit
+ *   integer M_k = m_k 2^(7 - E_k) and E = max_k E_k,
+ *   S = sum_k M_k^p 2^(24 - p (E - E_k)) over the terms with
+ *   p (E - E_k) <= 24 (an exact integer), and
+ *   rho = fl(c / r) * 2^(24/p + 7 - E), r = fl(fl(S)/K) (p = 1) or
+ *   fl(sqrt(fl(fl(S)/K))) (p = 2); this is c ((1/K) sum m_k^p)^(-1/p).
+ *   An all-zero row has no RMS to estimate: rho = +Inf, and its y (0 * Inf)
+ *   is NaN, so all its scales are 0xFF.  NaN/Inf rows as in mxnorm_fwd.
+ *   source : MXQ_SRC_SCALES or MXQ_SRC_ABSMAX
+ *   c      : 0 selects mxnorm_default_c_for(p, source)
+ *   had    : 0 (no rotation), 16 or 32 (as mxnorm_hadamard_fwd)
+ *   other arguments as mxnorm_fwd
+ */
+mxq_status mxnorm_fwd_ex(const void *x, const void *gamma, int64_t rows, int64_t hidden,
+                         int p, float c, mxq_source source, int had, mxq_elem elem,
+                         uint8_t *codes, uint8_t *scales, float *rrms, mxq_stream_t stream);
 
 /*
  * rmsnorm_mxquant_fwd -- the two-pass pipeline MXNorm replaces ([P1] §1:
@@ -178,6 +207,15 @@ size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
  * "Fundamentos Teoricos").  Returns 0 for p outside {1, 2}.
  */
 float mxnorm_default_c(int p);
+
+/*
+ * mxnorm_default_c_for -- host function.  Default c for either block
+ * magnitude: mxnorm_default_c(p) for MXQ_SRC_SCALES; for MXQ_SRC_ABSMAX,
+ * c = E[M^p]^(1/p) with M the max of 32 i.i.d. |N(0,1)| (2.3470793 for p = 1,
+ * 2.3894572 for p = 2), which makes c E[m^p]^(-1/p) = 1/RMS for Gaussian
+ * rows.  Returns 0 for p or source out of range.
+ */
+float mxnorm_default_c_for(int p, mxq_source source);
 
 /* mxq_status_str -- host function: a static, human-readable status name. */
 const char *mxq_status_str(mxq_status s);

@@ -16,13 +16,16 @@ import os
 import torch
 
 __all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
-           "mxnorm_bwd", "mxnorm_bwd_workspace_bytes",
+           "mxnorm_bwd", "mxnorm_bwd_workspace_bytes", "mxnorm_fwd_ex", "SRC_SCALES",
+           "SRC_ABSMAX",
            "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
            "library_path"]
 
 E4M3 = 0
 E2M1 = 1
 BLOCK = 32
+SRC_SCALES = 0   # block magnitude = the E8M0 scale as a power of two (mxnorm_fwd)
+SRC_ABSMAX = 1   # block magnitude = the exact block absmax
 MAX_HIDDEN = 32768
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +65,10 @@ def lib():
         L.mxnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
         L.mxnorm_bwd_workspace_bytes.restype = C.c_size_t
         L.mxnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+        L.mxnorm_fwd_ex.restype = i32
+        L.mxnorm_fwd_ex.argtypes = [vp, vp, i64, i64, i32, f32, i32, i32, i32, vp, vp, vp, vp]
+        L.mxnorm_default_c_for.restype = f32
+        L.mxnorm_default_c_for.argtypes = [i32, i32]
         L.mxnorm_default_c.restype = f32
         L.mxnorm_default_c.argtypes = [i32]
         L.mxq_status_str.restype = C.c_char_p
@@ -76,8 +83,8 @@ def status_str(status: int) -> str:
     return lib().mxq_status_str(status).decode()
 
 
-def mxnorm_default_c(p: int) -> float:
-    return float(lib().mxnorm_default_c(int(p)))
+def mxnorm_default_c(p: int, source: int = SRC_SCALES) -> float:
+    return float(lib().mxnorm_default_c_for(int(p), int(source)))
 
 
 def _check(status: int, name: str):
@@ -163,6 +170,21 @@ def mxnorm_hadamard_fwd(x, gamma=None, p=2, c=0.0, had=16, elem=E2M1, codes=None
     _check(lib().mxnorm_hadamard_fwd(_ptr(x), _ptr(gamma), rows, hidden, p, c, had, elem,
                                      _ptr(codes), _ptr(scales), _ptr(rrms), _stream(stream)),
            "mxnorm_hadamard_fwd")
+    return codes, scales, rrms
+
+
+def mxnorm_fwd_ex(x, gamma=None, p=2, c=0.0, source=SRC_SCALES, had=0, elem=E4M3, codes=None,
+                  scales=None, rrms=None, want_rrms=True, stream=None):
+    """MXNorm forward with a choice of block magnitude (and optional rotation)."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    gamma = _gamma(gamma, hidden)
+    codes, scales = _outputs(x, elem, codes, scales)
+    if rrms is None and want_rrms:
+        rrms = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(lib().mxnorm_fwd_ex(_ptr(x), _ptr(gamma), rows, hidden, p, c, source, had, elem,
+                               _ptr(codes), _ptr(scales), _ptr(rrms), _stream(stream)),
+           "mxnorm_fwd_ex")
     return codes, scales, rrms
 
 

@@ -13,7 +13,8 @@ struct MxnormArgs {
   int hidden;
   int p;
   float c;
-  int had;   // 0, 16 or 32
+  int had;     // 0, 16 or 32
+  int source;  // 0: E8M0-scale block magnitudes, 1: exact block absmax
   int elem;  // 0 = E4M3, 1 = E2M1
   uint8_t* codes;
   uint8_t* scales;

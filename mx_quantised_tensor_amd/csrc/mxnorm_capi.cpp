@@ -18,6 +18,9 @@ namespace {
 // 32 i.i.d. |N(0,1)| (E[M] = 2.3470792, E[M^2] = 5.7095053), rounded to fp32.
 constexpr float kDefaultC1 = 0x1.b16c5ep+0f;  // 1.6930598
 constexpr float kDefaultC2 = 0x1.c1ed54p+0f;  // 1.7575276
+// Exact block absmax: c = E[M^p]^(1/p), rounded to fp32.
+constexpr float kDefaultAbsC1 = 0x1.2c6d18p+1f;  // 2.3470793
+constexpr float kDefaultAbsC2 = 0x1.31d9bcp+1f;  // 2.3894572
 
 // Limits per call that keep every launch below 2^32 threads (a workgroup of
 // 256 threads per row at most; one thread per 8 elements at most).
@@ -44,11 +47,12 @@ mxq_status check_mx_outputs(const void* x, const uint8_t* codes, const uint8_t* 
 mxq_status status_of(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
 
 mxq_status mxnorm_common(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
-                         float c, int had, mxq_elem elem, uint8_t* codes, uint8_t* scales,
-                         float* rrms, mxq_stream_t stream) {
+                         float c, mxq_source source, int had, mxq_elem elem, uint8_t* codes,
+                         uint8_t* scales, float* rrms, mxq_stream_t stream) {
   mxq_status st = check_shape(rows, hidden, elem);
   if (st != MXQ_OK) return st;
   if (p != 1 && p != 2) return MXQ_EINVAL;
+  if (source != MXQ_SRC_SCALES && source != MXQ_SRC_ABSMAX) return MXQ_EINVAL;
   if (!(c >= 0.0f) || !isfinite(c)) return MXQ_EINVAL;
   if (had != 0 && had != 16 && had != 32) return MXQ_EINVAL;
   if (rows == 0) return MXQ_OK;
@@ -62,8 +66,9 @@ mxq_status mxnorm_common(const void* x, const void* gamma, int64_t rows, int64_t
   a.rows = rows;
   a.hidden = (int)hidden;
   a.p = p;
-  a.c = c == 0.0f ? mxnorm_default_c(p) : c;
+  a.c = c == 0.0f ? mxnorm_default_c_for(p, source) : c;
   a.had = had;
+  a.source = (int)source;
   a.elem = (int)elem;
   a.codes = codes;
   a.scales = scales;
@@ -91,14 +96,23 @@ mxq_status mx_quant(const void* x, int64_t rows, int64_t hidden, mxq_elem elem, 
 mxq_status mxnorm_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
                       float c, mxq_elem elem, uint8_t* codes, uint8_t* scales, float* rrms,
                       mxq_stream_t stream) {
-  return mxnorm_common(x, gamma, rows, hidden, p, c, 0, elem, codes, scales, rrms, stream);
+  return mxnorm_common(x, gamma, rows, hidden, p, c, MXQ_SRC_SCALES, 0, elem, codes, scales,
+                       rrms, stream);
 }
 
 mxq_status mxnorm_hadamard_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden,
                                int p, float c, int had, mxq_elem elem, uint8_t* codes,
                                uint8_t* scales, float* rrms, mxq_stream_t stream) {
   if (had != 16 && had != 32) return MXQ_EINVAL;
-  return mxnorm_common(x, gamma, rows, hidden, p, c, had, elem, codes, scales, rrms, stream);
+  return mxnorm_common(x, gamma, rows, hidden, p, c, MXQ_SRC_SCALES, had, elem, codes, scales,
+                       rrms, stream);
+}
+
+mxq_status mxnorm_fwd_ex(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
+                         float c, mxq_source source, int had, mxq_elem elem, uint8_t* codes,
+                         uint8_t* scales, float* rrms, mxq_stream_t stream) {
+  return mxnorm_common(x, gamma, rows, hidden, p, c, source, had, elem, codes, scales, rrms,
+                       stream);
 }
 
 mxq_status rmsnorm_mxquant_fwd(const void* x, const void* gamma, int64_t rows, int64_t hidden,
@@ -163,6 +177,14 @@ mxq_status mxnorm_bwd(const void* x, const void* dy, const void* gamma, const fl
 float mxnorm_default_c(int p) {
   if (p == 1) return kDefaultC1;
   if (p == 2) return kDefaultC2;
+  return 0.0f;
+}
+
+float mxnorm_default_c_for(int p, mxq_source source) {
+  if (source == MXQ_SRC_SCALES) return mxnorm_default_c(p);
+  if (source != MXQ_SRC_ABSMAX) return 0.0f;
+  if (p == 1) return kDefaultAbsC1;
+  if (p == 2) return kDefaultAbsC2;
   return 0.0f;
 }
 

@@ -65,39 +65,68 @@ __device__ __forceinline__ void store_codes_stream(uint8_t* __restrict__ dst, co
 }
 
 // ---- the MXNorm row statistic ([P1] §2 "Formula"; [P2] abstract) -----------------
-// Block magnitude: mt_k = 2^(e_k + emax) where e_k is the E8M0 exponent the MX
-// cast of x gives block k.  From the bf16 exponent field f of the block
-// absmax, e_k + emax + 127 = max(f, emax) (the E8M0 clamp at -127 included);
+// Two readings of the block magnitude mt_k (SRC):
+//   kSrcScales: mt_k = 2^(e_k + emax), e_k the E8M0 exponent the MX cast of x
+//     gives block k.  From the bf16 exponent field f of the block absmax,
+//     u = e_k + emax + 127 = max(f, emax) (the E8M0 clamp at -127 included).
+//   kSrcAbsmax: mt_k = the block absmax m_k itself = M_k * 2^(u - 134) with
+//     u = max(f, 1) and the 8-bit integer M_k = f ? 128 + fraction : fraction.
 // u = 255 marks a block holding NaN or Inf.
-template <int EMAX>
-__device__ __forceinline__ int block_u(const uint4 v) {
+constexpr int kSrcScales = 0;
+constexpr int kSrcAbsmax = 1;
+
+template <int SRC, int EMAX>
+__device__ __forceinline__ int block_u(const uint4 v, int& mp, int p_shift) {
   const uint32_t m = quad_max_u32(absmax8_bf16_bits(v));
-  return max((int)(m >> 7), EMAX);
+  const int f = (int)(m >> 7);
+  if constexpr (SRC == kSrcScales) {
+    (void)p_shift;
+    mp = 1;
+    return max(f, EMAX);
+  } else {
+    const int M = (int)(m & 0x7F) | (f != 0 ? 0x80 : 0);
+    mp = p_shift ? M * M : M;
+    return max(f, 1);
+  }
 }
 
-// The terms of S = sum_k 2^(40 - p (E1 - u_k)) with p (E1 - u_k) <= 40, as
-// exact doubles: the double whose high word is (1063 - t) << 20 (low word 0)
-// is 2^(40 - t).  S < 2^53, so summing these in fp64 is exact in any order.
+// The terms of the exact power sum, as doubles built from their exponent:
+//   kSrcScales: S = sum_k 2^(40 - t_k), t_k = p (E1 - u_k) <= 40;
+//   kSrcAbsmax: S = sum_k M_k^p 2^(24 - t_k), t_k <= 24.
+// The double whose high word is (1023 + W - t) << 20 (low word 0) is 2^(W - t);
+// M_k^p < 2^16, so every term is exact, and S < 2^53 (K <= 1024): summing the
+// terms in fp64 is exact in any order.
+template <int SRC>
 struct PowerSum {
-  int hbase;  // (1063 << 20) - (E1 << pk)
-  int umin;   // E1 - 40/p
+  static constexpr int kW = SRC == kSrcScales ? 40 : 24;
+  int hbase;  // ((1023 + W) << 20) - (E1 << pk)
+  int umin;   // E1 - W/p
   int pk;     // 20 + (p - 1): (p (E1 - u)) << 20 == (E1 - u) << pk for p in {1, 2}
   __device__ __forceinline__ PowerSum(int E1, int p_shift) {
     pk = 20 + p_shift;
-    hbase = (1063 << 20) - (E1 << pk);
-    umin = E1 - (40 >> p_shift);
+    hbase = ((1023 + kW) << 20) - (E1 << pk);
+    umin = E1 - (kW >> p_shift);
   }
-  __device__ __forceinline__ double term(int u) const {
-    return __hiloint2double(u >= umin ? hbase + (u << pk) : 0, 0);
+  __device__ __forceinline__ double term(int u, int mp) const {
+    const double pw = __hiloint2double(u >= umin ? hbase + (u << pk) : 0, 0);
+    if constexpr (SRC == kSrcScales) {
+      (void)mp;
+      return pw;
+    } else {
+      return pw * (double)mp;
+    }
   }
 };
 
-// rho = fl(c / r) * 2^(40/p - E), r = fl(fl(S)/K) (p = 1) or fl(sqrt(fl(fl(S)/K))),
-// E = E1 - 127.  Each step is one correctly rounded fp32 operation, evaluated in
-// fp64 and rounded once: a double result of +, *, /, sqrt on floats rounds to
-// the correctly rounded float (53 >= 2*24 + 2).  S * (1/K) in fp64 rounds to the
+// rho = fl(c / r) * 2^shift, r = fl(fl(S)/K) (p = 1) or fl(sqrt(fl(fl(S)/K))),
+// shift = 40/p - (E1 - 127) (kSrcScales) or 24/p + 7 - (E1 - 127) (kSrcAbsmax).
+// Each step is one correctly rounded fp32 operation, evaluated in fp64 and
+// rounded once: a double result of +, *, /, sqrt on floats rounds to the
+// correctly rounded float (53 >= 2*24 + 2).  S * (1/K) in fp64 rounds to the
 // same float as S / K: a 24-bit S divided by K <= 2^10 is never within 2^-52 of
-// a float rounding boundary.  E1 == 255 (NaN/Inf in the row) gives NaN.
+// a float rounding boundary.  E1 == 255 (NaN/Inf in the row) gives NaN; S == 0
+// (an all-zero row, absmax reading) gives +Inf.
+template <int SRC>
 __device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, float c,
                                                double inv_k) {
   if (E1 >= 255) return __uint_as_float(0x7FC00000u);
@@ -105,7 +134,9 @@ __device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, fl
   const float mu = (float)((double)Sf * inv_k);
   const float r = p_shift == 0 ? mu : (float)sqrt((double)mu);
   const float q = (float)((double)c / (double)r);
-  return (float)ldexp((double)q, (40 >> p_shift) - (E1 - 127));
+  const int shift = SRC == kSrcScales ? (40 >> p_shift) - (E1 - 127)
+                                      : (24 >> p_shift) + 7 - (E1 - 127);
+  return (float)ldexp((double)q, shift);
 }
 
 // ---- normalise (+gain), rotate, re-derive the block scale from y, cast ----------
@@ -158,7 +189,7 @@ struct WaveArgs {
 };
 
 // The whole forward of one row held in VGPRs (v: the row, gr: the gain).
-template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL>
+template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lane,
                                          const bool (&act)[STEPS], const uint4 (&v)[STEPS],
                                          const uint4 (&gr)[GAMMA ? STEPS : 1],
@@ -166,11 +197,11 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   const int K = a.hidden >> 5;
-  int u[STEPS];
+  int u[STEPS], mp[STEPS];
   int umax = kInactive;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    int us = block_u<EMAX>(v[s]);
+    int us = block_u<SRC, EMAX>(v[s], mp[s], a.p_shift);
     if constexpr (!FULL) us = act[s] ? us : kInactive;
     u[s] = us;
     umax = max(umax, us);
@@ -179,12 +210,12 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
 
   float rho;
   {
-    const PowerSum ps(E1, a.p_shift);
+    const PowerSum<SRC> ps(E1, a.p_shift);
     double S = 0.0;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) S += ps.term(u[s]);
+    for (int s = 0; s < STEPS; ++s) S += ps.term(u[s], mp[s]);
     S = wave_sum_quads_f64(S);
-    rho = rho_from_stat(E1, S, a.p_shift, a.c, a.inv_k);
+    rho = rho_from_stat<SRC>(E1, S, a.p_shift, a.c, a.inv_k);
   }
   if (a.rrms != nullptr && lane == 0) a.rrms[row] = rho;
 
@@ -223,7 +254,7 @@ __device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[ST
   }
 }
 
-template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL>
+template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
   const int lane = threadIdx.x & 63;
@@ -247,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   } else {
     gr[0] = make_uint4(0, 0, 0, 0);
   }
-  wave_row<ELEM, GAMMA, HAD, STEPS, FULL>(a, row, lane, act, v, gr, s_sc[wave]);
+  wave_row<ELEM, GAMMA, HAD, STEPS, FULL, SRC>(a, row, lane, act, v, gr, s_sc[wave]);
 }
 
 // ----------------------------------------------------------------------------------
@@ -255,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
 // waves (4/W rows per workgroup); the two row reductions cross waves through
 // LDS.  Lane `lane` of wave `wir` owns chunk (s*W + wir)*64 + lane at step s.
 // ----------------------------------------------------------------------------------
-template <int ELEM, bool GAMMA, int HAD, int W, int STEPS>
+template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_wide(const WaveArgs a) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
@@ -285,11 +316,11 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wide(const WaveArgs a) {
     v[s] = load_stream16(xrow + choff[s]);
   }
 
-  int u[STEPS];
+  int u[STEPS], mp[STEPS];
   int umax = kInactive;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int us = block_u<EMAX>(v[s]);
+    const int us = block_u<SRC, EMAX>(v[s], mp[s], a.p_shift);
     u[s] = act[s] ? us : kInactive;
     umax = max(umax, u[s]);
   }
@@ -300,17 +331,17 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wide(const WaveArgs a) {
 #pragma unroll
   for (int w = 1; w < W; ++w) E1 = max(E1, s_max[rslot * W + w]);
 
-  const PowerSum ps(E1, a.p_shift);
+  const PowerSum<SRC> ps(E1, a.p_shift);
   double S = 0.0;
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) S += ps.term(u[s]);
+  for (int s = 0; s < STEPS; ++s) S += ps.term(u[s], mp[s]);
   S = wave_sum_quads_f64(S);
   if (lane == 0) s_sum[wave] = S;
   __syncthreads();
   S = s_sum[rslot * W];
 #pragma unroll
   for (int w = 1; w < W; ++w) S += s_sum[rslot * W + w];
-  const float rho = rho_from_stat(E1, S, a.p_shift, a.c, a.inv_k);
+  const float rho = rho_from_stat<SRC>(E1, S, a.p_shift, a.c, a.inv_k);
   if (a.rrms != nullptr && row_ok && wir == 0 && lane == 0) a.rrms[row] = rho;
 
   uint8_t* crow = a.codes + row * (int64_t)(ELEM == 0 ? a.hidden : a.hidden / 2);
@@ -474,47 +505,53 @@ WaveArgs wave_args(const MxnormArgs& m) {
   return a;
 }
 
-template <int ELEM, bool GAMMA, int HAD, int STEPS>
+template <int ELEM, bool GAMMA, int HAD, int SRC, int STEPS>
 hipError_t launch_wave(const MxnormArgs& m) {
   const WaveArgs a = wave_args(m);
   const dim3 grid((unsigned)((m.rows + 3) / 4));
   if (m.hidden == 512 * STEPS)
-    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, true>), grid, dim3(kThreads), 0,
-                       (hipStream_t)m.stream, a);
+    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, true, SRC>), grid,
+                       dim3(kThreads), 0, (hipStream_t)m.stream, a);
   else
-    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, false>), grid, dim3(kThreads), 0,
-                       (hipStream_t)m.stream, a);
+    hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, false, SRC>), grid,
+                       dim3(kThreads), 0, (hipStream_t)m.stream, a);
   return hipGetLastError();
 }
 
-template <int ELEM, bool GAMMA, int HAD, int W, int STEPS>
+template <int ELEM, bool GAMMA, int HAD, int SRC, int W, int STEPS>
 hipError_t launch_wide(const MxnormArgs& m) {
   const WaveArgs a = wave_args(m);
   const dim3 grid((unsigned)((m.rows + (4 / W) - 1) / (4 / W)));
-  hipLaunchKernelGGL((k_mxnorm_wide<ELEM, GAMMA, HAD, W, STEPS>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((k_mxnorm_wide<ELEM, GAMMA, HAD, W, STEPS, SRC>), grid, dim3(kThreads), 0,
                      (hipStream_t)m.stream, a);
   return hipGetLastError();
 }
 
-template <int ELEM, bool GAMMA, int HAD>
+template <int ELEM, bool GAMMA, int HAD, int SRC>
 hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   const RowShape r = pick_row_shape(m.hidden);
-  if (r.waves == 1 && r.steps == 1) return launch_wave<ELEM, GAMMA, HAD, 1>(m);
-  if (r.waves == 1 && r.steps == 2) return launch_wave<ELEM, GAMMA, HAD, 2>(m);
-  if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, 4>(m);
-  if (r.waves == 1 && r.steps == 8) return launch_wave<ELEM, GAMMA, HAD, 8>(m);
-  if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, 2, 8>(m);
-  if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, 4, 8>(m);
-  if (r.waves == 4 && r.steps == 16) return launch_wide<ELEM, GAMMA, HAD, 4, 16>(m);
+  if (r.waves == 1 && r.steps == 1) return launch_wave<ELEM, GAMMA, HAD, SRC, 1>(m);
+  if (r.waves == 1 && r.steps == 2) return launch_wave<ELEM, GAMMA, HAD, SRC, 2>(m);
+  if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
+  if (r.waves == 1 && r.steps == 8) return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
+  if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
+  if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
+  if (r.waves == 4 && r.steps == 16) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 16>(m);
   return hipErrorInvalidValue;
+}
+
+template <int ELEM, bool GAMMA, int HAD>
+hipError_t launch_mxnorm_src(const MxnormArgs& m) {
+  return m.source == kSrcScales ? launch_mxnorm_shape<ELEM, GAMMA, HAD, kSrcScales>(m)
+                                : launch_mxnorm_shape<ELEM, GAMMA, HAD, kSrcAbsmax>(m);
 }
 
 template <int ELEM, bool GAMMA>
 hipError_t launch_mxnorm_had(const MxnormArgs& m) {
   switch (m.had) {
-    case 0: return launch_mxnorm_shape<ELEM, GAMMA, 0>(m);
-    case 16: return launch_mxnorm_shape<ELEM, GAMMA, 16>(m);
-    case 32: return launch_mxnorm_shape<ELEM, GAMMA, 32>(m);
+    case 0: return launch_mxnorm_src<ELEM, GAMMA, 0>(m);
+    case 16: return launch_mxnorm_src<ELEM, GAMMA, 16>(m);
+    case 32: return launch_mxnorm_src<ELEM, GAMMA, 32>(m);
     default: return hipErrorInvalidValue;
   }
 }

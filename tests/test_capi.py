@@ -29,9 +29,9 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mxq.lib()
     names = declared_functions()
-    assert set(names) >= {"mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd",
+    assert set(names) >= {"mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd", "mxnorm_fwd_ex",
                           "rmsnorm_mxquant_fwd", "mxnorm_bwd", "mxnorm_bwd_workspace_bytes",
-                          "mxnorm_default_c", "mxq_status_str"}
+                          "mxnorm_default_c", "mxnorm_default_c_for", "mxq_status_str"}
     for n in names:
         assert hasattr(L, n), n
     assert mxq.lib().mxq_version().decode().startswith("mxnorm-gfx950")
@@ -41,7 +41,29 @@ def test_default_c_matches_derivation():
     for p in (1, 2):
         want = np.float32(derive_c.c_pow2_scale(p))
         assert np.float32(mxq.mxnorm_default_c(p)) == want
+        assert np.float32(mxq.lib().mxnorm_default_c(p)) == want
+        want = np.float32(derive_c.c_exact_absmax(p))
+        assert np.float32(mxq.mxnorm_default_c(p, mxq.SRC_ABSMAX)) == want
     assert mxq.mxnorm_default_c(3) == 0.0
+    assert mxq.mxnorm_default_c(2, 2) == 0.0
+
+
+def _ex(source=0, had=0, **kw):
+    a = dict(x=A16, g=None, rows=4, hidden=64, p=2, c=0.0, elem=0, codes=A16, scales=A16,
+             rrms=None)
+    a.update(kw)
+    return mxq.lib().mxnorm_fwd_ex(a["x"], a["g"], a["rows"], a["hidden"], a["p"], a["c"], source,
+                                   had, a["elem"], a["codes"], a["scales"], a["rrms"], None)
+
+
+def test_fwd_ex_argument_checks():
+    assert _ex(source=2) == EINVAL
+    assert _ex(source=-1) == EINVAL
+    assert _ex(source=1, had=8) == EINVAL
+    assert _ex(source=1, p=3) == EINVAL
+    assert _ex(source=1, hidden=48) == EINVAL
+    assert _ex(source=1, x=MIS) == EALIGN
+    assert _ex(source=1, rows=0, x=None, codes=None, scales=None) == OK
 
 
 def test_status_strings():
