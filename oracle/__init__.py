@@ -75,6 +75,15 @@ def lib():
         L.mxo_max_threads.restype = C.c_int
         L.mxo_max_threads.argtypes = []
         f64p = C.POINTER(C.c_double)
+        L.mxo_mx_quant_gain.restype = C.c_int
+        L.mxo_mx_quant_gain.argtypes = [u16p, u16p, i64, i64, C.c_int, u8p, u8p]
+        L.mxo_mx_dot.restype = C.c_double
+        L.mxo_mx_dot.argtypes = [u8p, u8p, u8p, u8p, i64]
+        L.mxo_mx_matmul.restype = C.c_int
+        L.mxo_mx_matmul.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, f64p]
+        L.mxo_mx_matmul_sampled.restype = C.c_int
+        L.mxo_mx_matmul_sampled.argtypes = [u8p, u8p, u8p, u8p, i64, C.POINTER(C.c_int64), i64,
+                                            f64p]
         L.mxo_mxnorm_fwd_ex.restype = C.c_int
         L.mxo_mxnorm_fwd_ex.argtypes = [u16p, u16p, i64, i64, C.c_int, C.c_float, C.c_int,
                                         C.c_int, C.c_int, u8p, u8p, f32p]
@@ -281,3 +290,45 @@ def row_stat_absmax(xrow, p):
 
 def rho_absmax(E, S, K, p, c):
     return float(np.float32(lib().mxo_rho_absmax(E, S, K, p, c)))
+
+
+def mx_quant_gain(w, gamma, elem):
+    """MX cast of the gain-folded weight fl32(W * gamma) (MXNormLinear)."""
+    w = _bf16(w)
+    rows, hidden = w.shape
+    g = _bf16(gamma)
+    codes = np.zeros((rows, codes_cols(hidden, elem)), dtype=np.uint8)
+    scales = np.zeros((rows, hidden // BLOCK), dtype=np.uint8)
+    _check(lib().mxo_mx_quant_gain(_ptr(w, C.c_uint16), _ptr(g, C.c_uint16), rows, hidden, elem,
+                                   _ptr(codes, C.c_uint8), _ptr(scales, C.c_uint8)),
+           "mx_quant_gain")
+    return codes, scales
+
+
+def _u8(a):
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def mx_matmul(a_codes, a_scales, b_codes, b_scales):
+    """fp64 C = A B^T for MXFP8 (E4M3) A [M, K] and B [N, K]."""
+    a_codes, a_scales, b_codes, b_scales = map(_u8, (a_codes, a_scales, b_codes, b_scales))
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    c = np.zeros((M, N), dtype=np.float64)
+    _check(lib().mxo_mx_matmul(_ptr(a_codes, C.c_uint8), _ptr(a_scales, C.c_uint8),
+                               _ptr(b_codes, C.c_uint8), _ptr(b_scales, C.c_uint8), M, N, K,
+                               _ptr(c, C.c_double)), "mx_matmul")
+    return c
+
+
+def mx_matmul_sampled(a_codes, a_scales, b_codes, b_scales, mn):
+    """fp64 C[m, n] for the listed (m, n) pairs only."""
+    a_codes, a_scales, b_codes, b_scales = map(_u8, (a_codes, a_scales, b_codes, b_scales))
+    K = a_codes.shape[1]
+    mn = np.ascontiguousarray(mn, dtype=np.int64).reshape(-1, 2)
+    out = np.zeros((mn.shape[0],), dtype=np.float64)
+    _check(lib().mxo_mx_matmul_sampled(_ptr(a_codes, C.c_uint8), _ptr(a_scales, C.c_uint8),
+                                       _ptr(b_codes, C.c_uint8), _ptr(b_scales, C.c_uint8), K,
+                                       mn.ctypes.data_as(C.POINTER(C.c_int64)), mn.shape[0],
+                                       _ptr(out, C.c_double)), "mx_matmul_sampled")
+    return out

@@ -652,6 +652,94 @@ int mxo_mxnorm_bwd(const uint16_t *x, const uint16_t *dy, const uint16_t *gamma,
 }
 
 /* ------------------------------------------------------------------------
+ * MXNormLinear (P1 §2 "Implementacion", MXNormLinear item: the gain is folded
+ * into the weights of the following linear layer, and that layer consumes
+ * the MX tensor MXNorm emits).
+ *
+ * mxo_mx_quant_gain: the folded weight W'[o, d] = W[o, d] * gamma[d] (a
+ * product of two bf16 values, exact in fp32), MX-cast along d exactly as
+ * mxo_mx_quant casts a matrix (scales per 32 consecutive d).
+ * ---------------------------------------------------------------------- */
+int mxo_mx_quant_gain(const uint16_t *w, const uint16_t *gamma, int64_t rows, int64_t hidden,
+                      int elem, uint8_t *codes, uint8_t *scales)
+{
+    if (check_shape(rows, hidden, elem) != MXO_OK || gamma == NULL)
+        return MXO_EINVAL;
+    build_tables();
+    const int64_t K = hidden / MXO_BLOCK, cpr = codes_per_row(hidden, elem);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float v[MXO_BLOCK];
+        for (int64_t k = 0; k < K; k++) {
+            for (int i = 0; i < MXO_BLOCK; i++) {
+                int64_t col = k * MXO_BLOCK + i;
+                v[i] = (float)mxo_bf16_decode(w[r * hidden + col]) *
+                       (float)mxo_bf16_decode(gamma[col]);
+            }
+            quantise_block(v, MXO_BLOCK, elem, codes + r * cpr, (int)(k * MXO_BLOCK),
+                           &scales[r * K + k]);
+        }
+    }
+    return MXO_OK;
+}
+
+/* Value of element k of an MXFP8 (E4M3) row: code * 2^(scale - 127); a 0xFF
+ * scale is NaN. */
+static double mx_e4m3_value(const uint8_t *codes, const uint8_t *scales, int64_t k)
+{
+    uint8_t s = scales[k / MXO_BLOCK];
+    if (s == 0xFF)
+        return NAN;
+    return ldexp(mxo_e4m3_decode(codes[k]), (int)s - 127);
+}
+
+/* Dot product of two MXFP8 rows of length K, in fp64 in index order. */
+double mxo_mx_dot(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                  const uint8_t *b_scales, int64_t K)
+{
+    build_tables();
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; k++)
+        acc += mx_e4m3_value(a_codes, a_scales, k) * mx_e4m3_value(b_codes, b_scales, k);
+    return acc;
+}
+
+/* C[m, n] = sum_k A[m, k] B[n, k] for MXFP8 A [M, K] and B [N, K] (both
+ * K-contiguous with scales [*, K/32]), in fp64. */
+int mxo_mx_matmul(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                  const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, double *c)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % MXO_BLOCK != 0)
+        return MXO_EINVAL;
+    build_tables();
+    const int64_t KB = K / MXO_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            c[m * N + n] = mxo_mx_dot(a_codes + m * K, a_scales + m * KB, b_codes + n * K,
+                                      b_scales + n * KB, K);
+    return MXO_OK;
+}
+
+/* The same for a list of (m, n) pairs only (large shapes, sampled outputs). */
+int mxo_mx_matmul_sampled(const uint8_t *a_codes, const uint8_t *a_scales,
+                          const uint8_t *b_codes, const uint8_t *b_scales, int64_t K,
+                          const int64_t *mn, int64_t count, double *out)
+{
+    if (K <= 0 || K % MXO_BLOCK != 0)
+        return MXO_EINVAL;
+    build_tables();
+    const int64_t KB = K / MXO_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; t++) {
+        int64_t m = mn[2 * t], n = mn[2 * t + 1];
+        out[t] = mxo_mx_dot(a_codes + m * K, a_scales + m * KB, b_codes + n * K,
+                            b_scales + n * KB, K);
+    }
+    return MXO_OK;
+}
+
+/* ------------------------------------------------------------------------
  * Bulk helpers used by the tests to pin the scalar routines over large sets.
  * ---------------------------------------------------------------------- */
 void mxo_bf16_encode_array(const float *f, int64_t n, uint16_t *out)

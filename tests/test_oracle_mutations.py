@@ -46,6 +46,12 @@ MUTATIONS = [
     ("absmax_drop_threshold", "if (t <= 24) {\n            uint64_t mp", "if (t <= 20) {\n            uint64_t mp"),
     ("absmax_exponent_offset", "return ldexpf(q, 24 / p + 7 - E);", "return ldexpf(q, 24 / p - E);"),
     ("absmax_power_ignored", "uint64_t mp = (p == 1) ? mk : mk * mk;", "uint64_t mp = mk;"),
+    # MXNormLinear pieces
+    ("matmul_scale_bias", "return ldexp(mxo_e4m3_decode(codes[k]), (int)s - 127);",
+     "return ldexp(mxo_e4m3_decode(codes[k]), (int)s - 128);"),
+    ("matmul_block_index", "uint8_t s = scales[k / MXO_BLOCK];", "uint8_t s = scales[k / (2 * MXO_BLOCK)];"),
+    ("gain_not_folded", "v[i] = (float)mxo_bf16_decode(w[r * hidden + col]) *\n                       (float)mxo_bf16_decode(gamma[col]);",
+     "v[i] = (float)mxo_bf16_decode(w[r * hidden + col]);"),
     ("absmax_no_subnormal_clamp", "if (e < -126)\n        e = -126;\n    *E_k = e;", "*E_k = e;"),
 ]
 
@@ -63,7 +69,8 @@ def _run_mutant(name, old, new, tmp):
     env = dict(os.environ, MXO_LIB=so_path, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_mxnorm.py",
-                        "tests/test_oracle_bwd.py", "tests/test_oracle_absmax.py"],
+                        "tests/test_oracle_bwd.py", "tests/test_oracle_absmax.py",
+                        "tests/test_oracle_linear.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode
 
