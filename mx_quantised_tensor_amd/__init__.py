@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
            "mxnorm_bwd", "mxnorm_bwd_workspace_bytes", "mxnorm_fwd_ex", "SRC_SCALES",
-           "SRC_ABSMAX",
+           "SRC_ABSMAX", "mx_quant_gain", "mx_matmul", "mxnorm_linear_fwd",
            "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
            "library_path"]
 
@@ -65,6 +65,12 @@ def lib():
         L.mxnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
         L.mxnorm_bwd_workspace_bytes.restype = C.c_size_t
         L.mxnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+        L.mx_quant_gain.restype = i32
+        L.mx_quant_gain.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+        L.mx_matmul.restype = i32
+        L.mx_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        L.mxnorm_linear_fwd.restype = i32
+        L.mxnorm_linear_fwd.argtypes = [vp, i64, i64, i32, f32, vp, vp, i64, vp, vp, vp, vp, vp]
         L.mxnorm_fwd_ex.restype = i32
         L.mxnorm_fwd_ex.argtypes = [vp, vp, i64, i64, i32, f32, i32, i32, i32, vp, vp, vp, vp]
         L.mxnorm_default_c_for.restype = f32
@@ -236,3 +242,57 @@ def mxnorm_bwd(x, dy, rrms, gamma=None, dx=None, dgamma=None, workspace=None, st
     _check(lib().mxnorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(rrms), rows, hidden, _ptr(dx),
                             _ptr(dgamma), _ptr(workspace), _stream(stream)), "mxnorm_bwd")
     return dx, dgamma
+
+
+def mx_quant_gain(w, gamma, elem=E4M3, codes=None, scales=None, stream=None):
+    """MX cast of the gain-folded weight fl32(W * gamma) -> (codes, scales)."""
+    w = _bf16_2d(w)
+    rows, hidden = w.shape
+    gamma = _gamma(gamma, hidden)
+    if gamma is None:
+        raise ValueError("mx_quant_gain needs a gain")
+    codes, scales = _outputs(w, elem, codes, scales)
+    _check(lib().mx_quant_gain(_ptr(w), _ptr(gamma), rows, hidden, elem, _ptr(codes),
+                               _ptr(scales), _stream(stream)), "mx_quant_gain")
+    return codes, scales
+
+
+def _u8_2d(t, name):
+    if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous 2-D uint8 device tensor" % name)
+    return t
+
+
+def mx_matmul(a_codes, a_scales, b_codes, b_scales, c=None, stream=None):
+    """C = A B^T (fp32) for MXFP8 A [M, K] and B [N, K]."""
+    a_codes, a_scales = _u8_2d(a_codes, "a_codes"), _u8_2d(a_scales, "a_scales")
+    b_codes, b_scales = _u8_2d(b_codes, "b_codes"), _u8_2d(b_scales, "b_scales")
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    if b_codes.shape[1] != K or a_scales.shape != (M, K // BLOCK) or \
+            b_scales.shape != (N, K // BLOCK):
+        raise ValueError("operand shapes do not agree")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(lib().mx_matmul(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+                           _ptr(c), _stream(stream)), "mx_matmul")
+    return c
+
+
+def mxnorm_linear_fwd(x, w_codes, w_scales, p=2, c=0.0, out=None, x_codes=None, x_scales=None,
+                      rrms=None, stream=None):
+    """MXNormLinear forward: mxnorm_fwd (no gain, E4M3) then mx_matmul with the
+    gain-folded MXFP8 weight -> (out fp32 [rows, out_features], x_codes, x_scales, rrms)."""
+    x = _bf16_2d(x)
+    rows, hidden = x.shape
+    w_codes, w_scales = _u8_2d(w_codes, "w_codes"), _u8_2d(w_scales, "w_scales")
+    O = w_codes.shape[0]
+    x_codes, x_scales = _outputs(x, E4M3, x_codes, x_scales)
+    if rrms is None:
+        rrms = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((rows, O), dtype=torch.float32, device=x.device)
+    _check(lib().mxnorm_linear_fwd(_ptr(x), rows, hidden, p, c, _ptr(w_codes), _ptr(w_scales), O,
+                                   _ptr(x_codes), _ptr(x_scales), _ptr(rrms), _ptr(out),
+                                   _stream(stream)), "mxnorm_linear_fwd")
+    return out, x_codes, x_scales, rrms

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmxnorm.so")
-SOURCES = ["mxnorm_kernels.hip", "mxnorm_bwd.hip", "mxnorm_capi.cpp"]
+SOURCES = ["mxnorm_kernels.hip", "mxnorm_bwd.hip", "mx_gemm.hip", "mxnorm_capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -29,6 +29,14 @@ hipError_t launch_mx_quant(const void* x, int64_t rows, int hidden, int elem, ui
 hipError_t launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int hidden, float eps,
                           void* y, float* rstd, void* stream);
 
+// MXFP8 x MXFP8 matrix product C[M, N] = A[M, K] B[N, K]^T (K % 128 == 0).
+hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                          const uint8_t* bs, int64_t M, int64_t N, int K, float* c,
+                          void* stream);
+// MX cast of fl32(w * gamma) along rows of w (the gain folded into a weight).
+hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,
+                                int elem, uint8_t* codes, uint8_t* scales, void* stream);
+
 // Straight-through MXNorm backward.  hidden <= kBwdMaxHidden.
 constexpr int kBwdMaxHidden = 4096;
 // Persistent workgroups of the backward with a gain (4 waves each); tuned on

@@ -26,6 +26,8 @@ constexpr float kDefaultAbsC2 = 0x1.31d9bcp+1f;  // 2.3894572
 // 256 threads per row at most; one thread per 8 elements at most).
 constexpr int64_t kMaxRows = ((int64_t)1 << 24) - 1;
 constexpr int64_t kMaxElems = (int64_t)1 << 34;
+// The matrix product advances K in stages of 128.
+constexpr int64_t kMatmulK = 128;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -133,6 +135,54 @@ mxq_status rmsnorm_mxquant_fwd(const void* x, const void* gamma, int64_t rows, i
   if (e != hipSuccess) return MXQ_EHIP;
   return status_of(
       mxq::launch_mx_quant(y_workspace, rows, (int)hidden, (int)elem, codes, scales, stream));
+}
+
+mxq_status mx_quant_gain(const void* w, const void* gamma, int64_t rows, int64_t hidden,
+                         mxq_elem elem, uint8_t* codes, uint8_t* scales, mxq_stream_t stream) {
+  mxq_status st = check_shape(rows, hidden, elem);
+  if (st != MXQ_OK) return st;
+  if (rows == 0) return MXQ_OK;
+  st = check_mx_outputs(w, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (gamma == nullptr) return MXQ_EINVAL;
+  if (!aligned(gamma, 16)) return MXQ_EALIGN;
+  (void)hipGetLastError();
+  return status_of(
+      mxq::launch_mx_quant_gain(w, gamma, rows, (int)hidden, (int)elem, codes, scales, stream));
+}
+
+mxq_status mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c,
+                     mxq_stream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % MXQ_BLOCK != 0) return MXQ_EINVAL;
+  if (K % kMatmulK != 0 || K > MXQ_MAX_HIDDEN * 4) return MXQ_EUNSUPPORTED;
+  if (M > kMaxRows * 4 || N > kMaxRows * 4) return MXQ_EUNSUPPORTED;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 31)) return MXQ_EUNSUPPORTED;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MXQ_EINVAL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(c, 4))
+    return MXQ_EALIGN;
+  (void)hipGetLastError();
+  return status_of(mxq::launch_mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, (int)K, c,
+                                       stream));
+}
+
+mxq_status mxnorm_linear_fwd(const void* x, int64_t rows, int64_t hidden, int p, float c,
+                             const uint8_t* w_codes, const uint8_t* w_scales,
+                             int64_t out_features, uint8_t* x_codes, uint8_t* x_scales,
+                             float* rrms, float* out, mxq_stream_t stream) {
+  mxq_status st = check_shape(rows, hidden, MXQ_E4M3);
+  if (st != MXQ_OK) return st;
+  if (p != 1 && p != 2) return MXQ_EINVAL;
+  if (!(c >= 0.0f) || !isfinite(c)) return MXQ_EINVAL;
+  if (out_features < 0) return MXQ_EINVAL;
+  if (hidden % kMatmulK != 0) return MXQ_EUNSUPPORTED;
+  if (rows == 0 || out_features == 0) return MXQ_OK;
+  st = mxnorm_common(x, nullptr, rows, hidden, p, c, MXQ_SRC_SCALES, 0, MXQ_E4M3, x_codes,
+                     x_scales, rrms, stream);
+  if (st != MXQ_OK) return st;
+  return mx_matmul(x_codes, x_scales, w_codes, w_scales, rows, out_features, hidden, out, stream);
 }
 
 size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {

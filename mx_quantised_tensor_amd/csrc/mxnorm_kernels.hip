@@ -379,6 +379,29 @@ __global__ __launch_bounds__(kThreads) void k_mx_quant(const uint4* __restrict__
   if ((threadIdx.x & 3) == 0) scales[ch >> 2] = (uint8_t)sb;
 }
 
+// The same cast of fl32(w * gamma[column]) ([P1] §2 "Implementacion",
+// MXNormLinear: the gain folded into the weights of the next linear layer).
+// A product of two bf16 values is exact in fp32.
+template <int ELEM>
+__global__ __launch_bounds__(kThreads) void k_mx_quant_gain(const uint4* __restrict__ w,
+                                                             const uint4* __restrict__ gamma,
+                                                             int64_t nchunks, int row_chunks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  constexpr int EMAX = Elem<ELEM>::kEmax;
+  const int64_t ch = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (ch >= nchunks) return;
+  float y[8], g[8];
+  widen8(w[ch], y);
+  widen8(gamma[ch % row_chunks], g);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = y[i] * g[i];
+  const uint32_t mb = quad_max_u32(absmax8_f32_bits(y));
+  const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
+  store_codes_stream<ELEM>(codes + ch * Elem<ELEM>::kCodeBytesPerLane, y, sb);
+  if ((threadIdx.x & 3) == 0) scales[ch >> 2] = (uint8_t)sb;
+}
+
 // ----------------------------------------------------------------------------------
 // RMSNorm, pass 1 of the two-pass baseline ([P1] §1): full-width fp32 sum of
 // squares, rstd = 1/sqrt(mean + eps), bf16 y written to memory.  Same row
@@ -589,6 +612,21 @@ hipError_t launch_mxnorm(const MxnormArgs& a) {
   if (a.elem == 0)
     return a.gamma ? launch_mxnorm_had<0, true>(a) : launch_mxnorm_had<0, false>(a);
   return a.gamma ? launch_mxnorm_had<1, true>(a) : launch_mxnorm_had<1, false>(a);
+}
+
+hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,
+                                int elem, uint8_t* codes, uint8_t* scales, void* stream) {
+  const int64_t nchunks = rows * (int64_t)(hidden / 8);
+  const int64_t grid = (nchunks + kThreads - 1) / kThreads;
+  if (elem == 0)
+    hipLaunchKernelGGL(k_mx_quant_gain<0>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, static_cast<const uint4*>(w),
+                       static_cast<const uint4*>(gamma), nchunks, hidden / 8, codes, scales);
+  else
+    hipLaunchKernelGGL(k_mx_quant_gain<1>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, static_cast<const uint4*>(w),
+                       static_cast<const uint4*>(gamma), nchunks, hidden / 8, codes, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_quant(const void* x, int64_t rows, int hidden, int elem, uint8_t* codes,

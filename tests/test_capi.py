@@ -31,7 +31,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd", "mxnorm_fwd_ex",
                           "rmsnorm_mxquant_fwd", "mxnorm_bwd", "mxnorm_bwd_workspace_bytes",
-                          "mxnorm_default_c", "mxnorm_default_c_for", "mxq_status_str"}
+                          "mxnorm_default_c", "mxnorm_default_c_for", "mxq_status_str",
+                          "mx_quant_gain", "mx_matmul", "mxnorm_linear_fwd"}
     for n in names:
         assert hasattr(L, n), n
     assert mxq.lib().mxq_version().decode().startswith("mxnorm-gfx950")
@@ -201,3 +202,24 @@ def test_python_binding_rejects_bad_tensors_on_cpu():
         mxq.mxnorm_fwd(x)          # host tensor
     with pytest.raises(TypeError):
         mxq.mx_quant(torch.zeros((4, 64), dtype=torch.float32))
+
+
+def _mm(a=A16, as_=A16, b=A16, bs=A16, M=128, N=128, K=256, c=A16):
+    return mxq.lib().mx_matmul(a, as_, b, bs, M, N, K, c, None)
+
+
+def test_matmul_argument_checks():
+    assert _mm(K=96) == EUNSUP          # a multiple of 32 but not of 128
+    assert _mm(K=100) == EINVAL
+    assert _mm(K=0) == EINVAL
+    assert _mm(M=-1) == EINVAL
+    assert _mm(M=0, a=None, as_=None, c=None) == OK
+    assert _mm(a=None) == EINVAL
+    assert _mm(a=MIS) == EALIGN
+    assert _mm(bs=A16 + 2) == EALIGN
+    assert _mm(c=A16 + 2) == EALIGN
+    L = mxq.lib()
+    assert L.mx_quant_gain(A16, None, 4, 64, 0, A16, A16, None) == EINVAL
+    assert L.mx_quant_gain(A16, MIS, 4, 64, 0, A16, A16, None) == EALIGN
+    assert L.mxnorm_linear_fwd(A16, 4, 96, 2, 0.0, A16, A16, 8, A16, A16, None, A16,
+                               None) == EUNSUP
