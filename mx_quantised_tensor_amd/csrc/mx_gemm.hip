@@ -21,13 +21,20 @@
 // the largest product (not an IEEE fp32 sum); successive instructions
 // accumulate in fp32.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C, each of its
-// 4 waves a 64 x 64 quarter (2 x 2 MFMA tiles).  K advances 128 bytes per
-// stage: the workgroup copies the 128 x 128-byte slices of A and B and their
-// scales into LDS (16-byte chunks XOR-swizzled by row so that the MFMA
-// fragment reads are free of bank conflicts) while holding the next stage's
-// data in registers.  Workgroups are remapped so that the tiles one XCD runs
-// share rows of A and columns of B in its L2.
+// Tiling.  A 256-thread workgroup (one wave per SIMD) owns 256 x 256 tiles of
+// C; each wave computes a 128 x 128 quarter as 4 x 4 MFMA tiles whose
+// accumulators live in AGPRs.  K advances 64 per stage (one MFMA k-step).
+// Each stage's slices of A and B (256 x 64 bytes each) and their scales are
+// copied from global memory straight into LDS by the gfx950 LDS-DMA loads,
+// into a ring of four buffers, up to four stages ahead of the one the waves
+// multiply.  16-byte chunks are
+// XOR-swizzled by row (applied on the global side of the copy) so that the
+// fragment reads are free of bank conflicts.  Fragment reads are
+// inline-assembly LDS loads with explicit waits, and the waits for the copies
+// are explicit vmcnt counts: the compiler cannot tell that an in-flight copy
+// writes another buffer and would otherwise wait for all of them before every
+// read.  Workgroups are persistent over tiles; tiles are taken in groups of 8
+// tile rows for L2 locality, each XCD a contiguous range.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,157 +45,260 @@ namespace mxq {
 namespace {
 
 constexpr int kGemmThreads = 256;
-constexpr int kTileM = 128;
-constexpr int kTileN = 128;
-constexpr int kStageK = 128;                   // bytes (= elements) of K per stage
-constexpr int kRowBytes = kStageK;             // LDS row: one stage of one row
-constexpr int kGroupM = 8;                     // tile rows per L2 group
+constexpr int kTile = 256;                      // C tile edge (rows and columns)
+constexpr int kStageK = 64;                     // K per stage (bytes = elements)
+constexpr int kRowBytes = kStageK;              // one row of a stage slice in LDS
+constexpr int kSlice = kTile * kRowBytes;       // 16 KiB: one operand's stage slice
+constexpr int kScaleBytes = kTile * 4;          // the aligned scale dword holding the stage
+constexpr int kBuf = 2 * kSlice + 2 * kScaleBytes;  // one stage buffer: A, B, scales
+constexpr int kRing = 4;                        // stage buffers (3 in flight)
+constexpr int kDmaOps = 10;                     // LDS-DMA instructions per wave per stage
+constexpr int kGroupM = 8;                      // tile rows per L2 group
 constexpr int kXcds = 8;
+constexpr int kMaxGroups = 256;                 // one persistent workgroup per CU
+
+#define MXQ_LDS __attribute__((address_space(3)))
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
-  const uint8_t* a;       // [M, K] E4M3
-  const uint8_t* as;      // [M, K/32] E8M0
-  const uint8_t* b;       // [N, K]
-  const uint8_t* bs;      // [N, K/32]
-  float* c;               // [M, N]
+  const uint8_t* a;   // [M, K] E4M3
+  const uint8_t* as;  // [M, K/32] E8M0
+  const uint8_t* b;   // [N, K]
+  const uint8_t* bs;  // [N, K/32]
+  float* c;           // [M, N]
   int64_t M, N;
   int K;
   int tiles_m, tiles_n;
 };
 
-// LDS offset of 16-byte chunk `chunk` (0..7) of row `row` in a stage slice.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+// In LDS, logical 16-byte chunk c (0..3) of row r of a slice is stored at
+// r * kRowBytes + ((c ^ ((r >> 1) & 3)) << 4): eight consecutive rows reading
+// the same logical chunk touch eight different 16-byte bank groups.
+
+__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+  v4i v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read1(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Tile t of the grouped order -> (tile row, tile column).
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (t / per_group) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int w = t % per_group;
+  tm = first_m + w % gm;
+  tn = w / gm;
+}
+
+// The DMA of one stage (k0) of the current tile into LDS at BUF: wave w copies
+// rows [64 w, 64 w + 64) of the A and B slices (4 x 1 KiB per operand: lane l
+// of copy q lands at row 64 w + 16 q + l/4, physical chunk l%4, and reads the
+// logical chunk that belongs there) and the two scale bytes of each of those
+// rows (the 4-byte-aligned scale word holding the stage's two blocks; LDS-DMA
+// writes 4 bytes per lane): kDmaOps instructions.  A macro: the LDS-DMA
+// builtin must sit in the kernel body itself.
+#define MXQ_GEMM_DMA(BUF, K0)                                                                 \
+  do {                                                                                        \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                           \
+      const int row = wave * 64 + q * 16 + (lane >> 2);                                       \
+      const int chunk = (lane & 3) ^ ((row >> 1) & 3);                                        \
+      const uint32_t dst = (BUF) + (uint32_t)((wave * 64 + q * 16) * kRowBytes);             \
+      __builtin_amdgcn_global_load_lds((const void*)(arow[q] + (K0) + chunk * 16),            \
+                                       (MXQ_LDS void*)(size_t)dst, 16, 0, 0);                 \
+      __builtin_amdgcn_global_load_lds((const void*)(brow[q] + (K0) + chunk * 16),            \
+                                       (MXQ_LDS void*)(size_t)(dst + kSlice), 16, 0, 0);      \
+    }                                                                                         \
+    __builtin_amdgcn_global_load_lds((const void*)(ascl + (((K0) >> 5) & ~3)),                \
+                                     (MXQ_LDS void*)(size_t)((BUF) + 2 * kSlice + wave * 256), \
+                                     4, 0, 0);                                                \
+    __builtin_amdgcn_global_load_lds(                                                         \
+        (const void*)(bscl + (((K0) >> 5) & ~3)),                                             \
+        (MXQ_LDS void*)(size_t)((BUF) + 2 * kSlice + kScaleBytes + wave * 256), 4, 0, 0);     \
+  } while (0)
+
+// This lane's fragments of tile pair i of one stage: A rows wm*128 + 32 i + fr
+// and B rows wn*128 + 32 i + fr, logical chunks fh (k-block 0 half) and 2 + fh
+// (k-block 1 half), and the scale byte of k-block fh of each of the two rows
+// (byte SB0 + fh of the row's scale word, SB0 = 0 or 2 by stage parity).
+#define MXQ_GEMM_READ(BUF, I, FA, FB, SA, SB, SB0)                                            \
+  do {                                                                                        \
+    FA[I][0] = lds_read16((BUF) + a_off[I] + c0);                                             \
+    FA[I][1] = lds_read16((BUF) + a_off[I] + c1);                                             \
+    FB[I][0] = lds_read16((BUF) + b_off[I] + c0);                                             \
+    FB[I][1] = lds_read16((BUF) + b_off[I] + c1);                                             \
+    SA[I] = lds_read1((BUF) + 2 * kSlice + (uint32_t)((wm * 128 + (I) * 32 + fr) * 4 + (SB0) + fh)); \
+    SB[I] = lds_read1((BUF) + 2 * kSlice + kScaleBytes +                                     \
+                      (uint32_t)((wn * 128 + (I) * 32 + fr) * 4 + (SB0) + fh));               \
+  } while (0)
+
+// Wait for this lane's fragment reads and make their registers visible as
+// written here (the compiler cannot see inside the reads).
+#define MXQ_GEMM_READ_WAIT(FA, FB, SA, SB)                                                    \
+  asm volatile("s_waitcnt lgkmcnt(0)"                                                         \
+               : "+v"(FA[0][0]), "+v"(FA[0][1]), "+v"(FA[1][0]), "+v"(FA[1][1]),             \
+                 "+v"(FA[2][0]), "+v"(FA[2][1]), "+v"(FA[3][0]), "+v"(FA[3][1]),             \
+                 "+v"(FB[0][0]), "+v"(FB[0][1]), "+v"(FB[1][0]), "+v"(FB[1][1]),             \
+                 "+v"(FB[2][0]), "+v"(FB[2][1]), "+v"(FB[3][0]), "+v"(FB[3][1]),             \
+                 "+v"(SA[0]), "+v"(SA[1]), "+v"(SA[2]), "+v"(SA[3]), "+v"(SB[0]),            \
+                 "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3]))
+
+// The 4 matrix instructions of A tile I of one stage, then an empty statement
+// taking their accumulators as inputs: it keeps them ahead of the volatile
+// LDS reads that follow (they touch no memory, so the compiler would
+// otherwise move them freely).
+#define MXQ_GEMM_MFMA_ROW(I, FA, FB, SA, SB)                                                  \
+  do {                                                                                        \
+    const v8i va = {FA[I][0].x, FA[I][0].y, FA[I][0].z, FA[I][0].w,                           \
+                    FA[I][1].x, FA[I][1].y, FA[I][1].z, FA[I][1].w};                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
+      const v8i vb = {FB[j][0].x, FB[j][0].y, FB[j][0].z, FB[j][0].w,                         \
+                      FB[j][1].x, FB[j][1].y, FB[j][1].z, FB[j][1].w};                        \
+      acc[I][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[I][j], 0, 0, 0, \
+                                                                  (int)SA[I], 0, (int)SB[j]); \
+    }                                                                                         \
+    asm volatile("" ::"a"(acc[I][0]), "a"(acc[I][1]), "a"(acc[I][2]), "a"(acc[I][3]));        \
+  } while (0)
+
 __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[kTileM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[kTileN * kRowBytes];
-  __shared__ uint32_t s_as[kTileM];  // the 4 block scales of the stage, per row
-  __shared__ uint32_t s_bs[kTileN];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kBuf];  // 132 KiB of 160
+  const uint32_t base = (uint32_t)(size_t)(MXQ_LDS uint8_t*)smem;
 
-  // ---- tile of this workgroup: XCD-contiguous ranges, grouped by kGroupM rows
-  // Workgroup bid runs on XCD bid % 8; when the tile count divides evenly,
-  // give each XCD a contiguous range of the grouped tile order.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // this wave's 128 x 128 quarter
+  const int fr = lane & 31;                 // fragment row / column within a 32-tile
+  const int fh = lane >> 5;                 // which 16-byte half of each k-block
+  const int KB = g.K >> 5;
+  const int nstages = g.K / kStageK;
   const int ntiles = g.tiles_m * g.tiles_n;
-  const int bid = blockIdx.x;
-  const int t = ntiles % kXcds == 0 ? (bid % kXcds) * (ntiles / kXcds) + bid / kXcds : bid;
-  const int group = t / (kGroupM * g.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(g.tiles_m - first_m, kGroupM);
-  const int tm = first_m + (t % (kGroupM * g.tiles_n)) % gm;
-  const int tn = (t % (kGroupM * g.tiles_n)) / gm;
-  const int64_t m0 = (int64_t)tm * kTileM;
-  const int64_t n0 = (int64_t)tn * kTileN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // this wave's 64 x 64 quarter
-  const int KB = g.K >> 5;                  // scale bytes per row
-
-  // ---- global -> register copy of one stage: thread `tid` moves the 16-byte
-  // chunk (tid & 7) of rows (tid >> 3) + 32 p, p = 0..3, of both A and B
-  const int crow = tid >> 3, cchunk = tid & 7;
-  const uint8_t* pa[4];
-  const uint8_t* pb[4];
+  // This lane's fragment rows inside a buffer.  Every such row is fr modulo 8,
+  // so logical chunk c sits at physical chunk c ^ ((fr >> 1) & 3).
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t ra = min(m0 + crow + 32 * p, g.M - 1);  // ragged tiles: clamp, mask later
-    const int64_t rb = min(n0 + crow + 32 * p, g.N - 1);
-    pa[p] = g.a + ra * g.K + cchunk * 16;
-    pb[p] = g.b + rb * g.K + cchunk * 16;
+  for (int i = 0; i < 4; ++i) {
+    a_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kRowBytes);
+    b_off[i] = kSlice + (uint32_t)((wn * 128 + i * 32 + fr) * kRowBytes);
   }
-  // scales: threads 0..127 fetch the A row's 4 stage scales, 128..255 B's
-  const bool sc_is_a = tid < kTileM;
-  const int srow = tid & (kTileM - 1);
-  const uint8_t* ps = sc_is_a ? g.as + min(m0 + srow, g.M - 1) * (int64_t)KB
-                              : g.bs + min(n0 + srow, g.N - 1) * (int64_t)KB;
+  const uint32_t c0 = (uint32_t)((fh ^ ((fr >> 1) & 3)) << 4);
+  const uint32_t c1 = (uint32_t)(((2 + fh) ^ ((fr >> 1) & 3)) << 4);
 
-  v4i ra[4], rb[4];
-  uint32_t rs;
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      ra[p] = *reinterpret_cast<const v4i*>(pa[p] + k0);
-      rb[p] = *reinterpret_cast<const v4i*>(pb[p] + k0);
+  // Tiles of this workgroup.  Workgroup bid runs on XCD bid % 8: when the
+  // counts allow, XCD x takes the contiguous range [x T/8, (x+1) T/8) of the
+  // grouped tile order, its G/8 workgroups interleaved over it.
+  const int G = (int)gridDim.x;
+  const bool by_xcd = ntiles % kXcds == 0 && G % kXcds == 0;
+  const int per_x = ntiles / kXcds, xcd = (int)blockIdx.x % kXcds, jx = (int)blockIdx.x / kXcds;
+  for (int it = 0;; ++it) {
+    int t;
+    if (by_xcd) {
+      const int w = jx + it * (G / kXcds);
+      if (w >= per_x) break;
+      t = xcd * per_x + w;
+    } else {
+      t = (int)blockIdx.x + it * G;
+      if (t >= ntiles) break;
     }
-    rs = *reinterpret_cast<const uint32_t*>(ps + (k0 >> 5));
-  };
-  auto stash = [&]() {
+    int tm, tn;
+    tile_coords(t, g.tiles_m, g.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+
+    // global sources of this wave's DMA rows (ragged tiles: clamped rows)
+    const uint8_t* arow[4];
+    const uint8_t* brow[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<v4i*>(s_a + lds_off(crow + 32 * p, cchunk)) = ra[p];
-      *reinterpret_cast<v4i*>(s_b + lds_off(crow + 32 * p, cchunk)) = rb[p];
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = wave * 64 + q * 16 + (lane >> 2);
+      arow[q] = g.a + min(m0 + r, g.M - 1) * (int64_t)g.K;
+      brow[q] = g.b + min(n0 + r, g.N - 1) * (int64_t)g.K;
     }
-    if (sc_is_a) s_as[srow] = rs; else s_bs[srow] = rs;
-  };
+    const uint8_t* ascl = g.as + min(m0 + wave * 64 + lane, g.M - 1) * (int64_t)KB;
+    const uint8_t* bscl = g.bs + min(n0 + wave * 64 + lane, g.N - 1) * (int64_t)KB;
 
-  v16f acc[2][2];
+    v16f acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int fr = lane & 31;   // fragment row (A) / column (B) within a 32-tile
-  const int fh = lane >> 5;   // which 16-byte halves of each k-block this lane holds
-  fetch(0);
-  for (int k0 = 0; k0 < g.K; k0 += kStageK) {
-    __syncthreads();  // the previous stage's fragment reads are done
-    stash();
-    __syncthreads();
-    if (k0 + kStageK < g.K) fetch(k0 + kStageK);  // in flight during the MFMAs
+    // Prologue: stages 0..3 in flight; wait for stage 0 (older vector-memory
+    // operations, such as the previous tile's C stores, retire first).
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
+    MXQ_GEMM_DMA(base, 0);
+    if (nstages > 1) MXQ_GEMM_DMA(base + kBuf, kStageK);
+    if (nstages > 2) MXQ_GEMM_DMA(base + 2 * kBuf, 2 * kStageK);
+    if (nstages > 3) MXQ_GEMM_DMA(base + 3 * kBuf, 3 * kStageK);
+    if (nstages > 3) wait_vmcnt<3 * kDmaOps>();
+    else if (nstages > 2) wait_vmcnt<2 * kDmaOps>();
+    else if (nstages > 1) wait_vmcnt<kDmaOps>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
 
-    uint32_t sa_w[2], sb_w[2];
+    // Stage s: read this stage's fragments, issue its 16 matrix instructions,
+    // wait for stage s + 1 to land in every wave; after that barrier every wave
+    // is done reading this stage's buffer, which then takes stage s + 4.
+    for (int s = 0; s < nstages; ++s) {
+      const uint32_t buf = base + (uint32_t)((s & 3) * kBuf);
+      v4i fa[4][2], fb[4][2];
+      uint32_t sa[4], sb[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      sa_w[i] = s_as[wm * 64 + i * 32 + fr];
-      sb_w[i] = s_bs[wn * 64 + i * 32 + fr];
-    }
+      for (int i = 0; i < 4; ++i) MXQ_GEMM_READ(buf, i, fa, fb, sa, sb, (2 * s) & 3);
+      MXQ_GEMM_READ_WAIT(fa, fb, sa, sb);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8i fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ar = wm * 64 + i * 32 + fr;
-        const int br = wn * 64 + i * 32 + fr;
-        const v4i a0 = *reinterpret_cast<const v4i*>(s_a + lds_off(ar, ks * 4 + fh));
-        const v4i a1 = *reinterpret_cast<const v4i*>(s_a + lds_off(ar, ks * 4 + 2 + fh));
-        const v4i b0 = *reinterpret_cast<const v4i*>(s_b + lds_off(br, ks * 4 + fh));
-        const v4i b1 = *reinterpret_cast<const v4i*>(s_b + lds_off(br, ks * 4 + 2 + fh));
-        fa[i] = (v8i){a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        fb[i] = (v8i){b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      }
-      // block (2 ks + fh) of the stage: lane i carries k-block 0's scale,
-      // lane i + 32 k-block 1's (byte 0 after the shift)
-      const int sh = 8 * (2 * ks + fh);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 0, 0, 0, (int)(sa_w[i] >> sh), 0, (int)(sb_w[j] >> sh));
-    }
-  }
-
-  // ---- epilogue: lane l, register r -> row (r%4) + 8(r/4) + 4(l/32), column l%32
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * fh;
-        if (row < g.M && col < g.N) g.c[row * g.N + col] = acc[i][j][r];
+      for (int i = 0; i < 4; ++i) MXQ_GEMM_MFMA_ROW(i, fa, fb, sa, sb);
+      if (s + 1 < nstages) {
+        // stages s+1 .. s+3 were issued; wait for s+1 (later ones may stay out)
+        if (s + 3 < nstages) wait_vmcnt<2 * kDmaOps>();
+        else if (s + 2 < nstages) wait_vmcnt<kDmaOps>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // also: every wave is done reading buffer s & 3
+        if (s + 4 < nstages) MXQ_GEMM_DMA(buf, (s + 4) * kStageK);
       }
     }
+
+    // epilogue: lane l, register r -> row (r%4) + 8(r/4) + 4(l/32), column l%32
+    const int64_t row0 = m0 + wm * 128 + 4 * fh, col0 = n0 + wn * 128 + fr;
+    if (m0 + kTile <= g.M && n0 + kTile <= g.N) {
+      float* cb = g.c + row0 * g.N + col0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* crow = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) crow[j * 32] = acc[i][j][r];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = col0 + j * 32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = row0 + i * 32 + (r & 3) + 8 * (r >> 2);
+            if (row < g.M && col < g.N) g.c[row * g.N + col] = acc[i][j][r];
+          }
+        }
+    }
+  }
 }
 
 }  // namespace
@@ -205,10 +315,11 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
   g.M = M;
   g.N = N;
   g.K = K;
-  g.tiles_m = (int)((M + kTileM - 1) / kTileM);
-  g.tiles_n = (int)((N + kTileN - 1) / kTileN);
-  const unsigned ntiles = (unsigned)g.tiles_m * (unsigned)g.tiles_n;
-  hipLaunchKernelGGL(k_mx_gemm, dim3(ntiles), dim3(kGemmThreads), 0, (hipStream_t)stream, g);
+  g.tiles_m = (int)((M + kTile - 1) / kTile);
+  g.tiles_n = (int)((N + kTile - 1) / kTile);
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int groups = ntiles < kMaxGroups ? ntiles : kMaxGroups;
+  hipLaunchKernelGGL(k_mx_gemm, dim3(groups), dim3(kGemmThreads), 0, (hipStream_t)stream, g);
   return hipGetLastError();
 }
 
