@@ -21,20 +21,27 @@
 // the largest product (not an IEEE fp32 sum); successive instructions
 // accumulate in fp32.
 //
-// Tiling.  A 256-thread workgroup (one wave per SIMD) owns 256 x 256 tiles of
-// C; each wave computes a 128 x 128 quarter as 4 x 4 MFMA tiles whose
-// accumulators live in AGPRs.  K advances 64 per stage (one MFMA k-step).
-// Each stage's slices of A and B (256 x 64 bytes each) and their scales are
-// copied from global memory straight into LDS by the gfx950 LDS-DMA loads,
-// into a ring of four buffers, up to four stages ahead of the one the waves
-// multiply.  16-byte chunks are
-// XOR-swizzled by row (applied on the global side of the copy) so that the
-// fragment reads are free of bank conflicts.  Fragment reads are
-// inline-assembly LDS loads with explicit waits, and the waits for the copies
-// are explicit vmcnt counts: the compiler cannot tell that an in-flight copy
-// writes another buffer and would otherwise wait for all of them before every
-// read.  Workgroups are persistent over tiles; tiles are taken in groups of 8
-// tile rows for L2 locality, each XCD a contiguous range.
+// Tiling.  A 256-thread workgroup (one wave per SIMD: the 256 accumulator
+// registers of a 128 x 128 quarter fill a lane's AGPRs) owns 256 x 256 tiles
+// of C; each wave computes its quarter as 4 x 4 matrix instructions per 64 k
+// (a "sub-stage").  Operands reach LDS by the gfx950 LDS-DMA buffer loads in
+// copy stages of 128 k: 128-byte row segments, one L2 line each, which the
+// memory path moves about 1.6x faster than 64-byte ones.  Two copy buffers
+// (2 x 64 KiB) alternate: stage j + 2 is copied while sub-stages 2j + 2 and
+// 2j + 3 multiply.  Block scales travel in 16-byte records per row (16
+// blocks = 4 copy stages), in three rotating sets, one small copy per stage.
+// The wave's fragments of sub-stage u + 1 are read from LDS into a second
+// register set while sub-stage u multiplies; LDS reads and copies are spread
+// between the 16 matrix instructions so that the in-order wave never stalls
+// its matrix unit behind a burst of memory instructions.  16-byte chunks are
+// XOR-swizzled by row (applied on the global side of the copy) and scale
+// records are rotated by row so that every LDS read is free of bank
+// conflicts.  Waits are explicit counts: the compiler cannot tell that an
+// in-flight copy writes the other buffer.  Rows beyond M or N fall outside
+// the buffer range and read as zero (their outputs are not stored).
+// Workgroups are persistent over tiles; tiles are taken in groups of 8 tile
+// rows for L2 locality, each XCD a contiguous range; C is written with
+// streaming (non-temporal) stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,13 +53,15 @@ namespace {
 
 constexpr int kGemmThreads = 256;
 constexpr int kTile = 256;                      // C tile edge (rows and columns)
-constexpr int kStageK = 64;                     // K per stage (bytes = elements)
-constexpr int kRowBytes = kStageK;              // one row of a stage slice in LDS
-constexpr int kSlice = kTile * kRowBytes;       // 16 KiB: one operand's stage slice
-constexpr int kScaleBytes = kTile * 4;          // the aligned scale dword holding the stage
-constexpr int kBuf = 2 * kSlice + 2 * kScaleBytes;  // one stage buffer: A, B, scales
-constexpr int kRing = 4;                        // stage buffers (3 in flight)
-constexpr int kDmaOps = 10;                     // LDS-DMA instructions per wave per stage
+constexpr int kCopyK = 128;                     // k per copy stage (= bytes per row)
+constexpr int kSlice = kTile * kCopyK;          // 32 KiB: one operand of one copy stage
+constexpr int kBuf = 2 * kSlice;                // 64 KiB: A and B of one copy stage
+constexpr int kScaleRec = 16;                   // one row's scale record: 16 blocks
+constexpr int kScaleSet = 2 * kTile * kScaleRec;  // 8 KiB: A and B records of a group
+constexpr int kScaleSets = 3;
+constexpr int kScaleBase = 2 * kBuf;
+constexpr int kLds = kScaleBase + kScaleSets * kScaleSet;  // 152 KiB of 160
+constexpr int kCopyOps = 18;                    // copy instructions per wave per stage
 constexpr int kGroupM = 8;                      // tile rows per L2 group
 constexpr int kXcds = 8;
 constexpr int kMaxGroups = 256;                 // one persistent workgroup per CU
@@ -62,6 +71,7 @@ constexpr int kMaxGroups = 256;                 // one persistent workgroup per 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 struct GemmArgs {
   const uint8_t* a;   // [M, K] E4M3
@@ -74,18 +84,20 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-// In LDS, logical 16-byte chunk c (0..3) of row r of a slice is stored at
-// r * kRowBytes + ((c ^ ((r >> 1) & 3)) << 4): eight consecutive rows reading
-// the same logical chunk touch eight different 16-byte bank groups.
+// Raw buffer of `bytes` bytes at p (stride 0, 32-bit data format): offsets at
+// or past `bytes` read as zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
   v4i v;
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
-__device__ __forceinline__ uint32_t lds_read1(uint32_t addr) {
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
   uint32_t v;
-  asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
 
@@ -94,6 +106,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// g mod 3 for 0 <= g < 2^14 without a division.
+__device__ __forceinline__ int mod3(int g) { return g - 3 * ((g * 0x5556) >> 16); }
 
 // Tile t of the grouped order -> (tile row, tile column).
 __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -105,77 +120,17 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   tn = w / gm;
 }
 
-// The DMA of one stage (k0) of the current tile into LDS at BUF: wave w copies
-// rows [64 w, 64 w + 64) of the A and B slices (4 x 1 KiB per operand: lane l
-// of copy q lands at row 64 w + 16 q + l/4, physical chunk l%4, and reads the
-// logical chunk that belongs there) and the two scale bytes of each of those
-// rows (the 4-byte-aligned scale word holding the stage's two blocks; LDS-DMA
-// writes 4 bytes per lane): kDmaOps instructions.  A macro: the LDS-DMA
-// builtin must sit in the kernel body itself.
-#define MXQ_GEMM_DMA(BUF, K0)                                                                 \
-  do {                                                                                        \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                           \
-      const int row = wave * 64 + q * 16 + (lane >> 2);                                       \
-      const int chunk = (lane & 3) ^ ((row >> 1) & 3);                                        \
-      const uint32_t dst = (BUF) + (uint32_t)((wave * 64 + q * 16) * kRowBytes);             \
-      __builtin_amdgcn_global_load_lds((const void*)(arow[q] + (K0) + chunk * 16),            \
-                                       (MXQ_LDS void*)(size_t)dst, 16, 0, 0);                 \
-      __builtin_amdgcn_global_load_lds((const void*)(brow[q] + (K0) + chunk * 16),            \
-                                       (MXQ_LDS void*)(size_t)(dst + kSlice), 16, 0, 0);      \
-    }                                                                                         \
-    __builtin_amdgcn_global_load_lds((const void*)(ascl + (((K0) >> 5) & ~3)),                \
-                                     (MXQ_LDS void*)(size_t)((BUF) + 2 * kSlice + wave * 256), \
-                                     4, 0, 0);                                                \
-    __builtin_amdgcn_global_load_lds(                                                         \
-        (const void*)(bscl + (((K0) >> 5) & ~3)),                                             \
-        (MXQ_LDS void*)(size_t)((BUF) + 2 * kSlice + kScaleBytes + wave * 256), 4, 0, 0);     \
-  } while (0)
-
-// This lane's fragments of tile pair i of one stage: A rows wm*128 + 32 i + fr
-// and B rows wn*128 + 32 i + fr, logical chunks fh (k-block 0 half) and 2 + fh
-// (k-block 1 half), and the scale byte of k-block fh of each of the two rows
-// (byte SB0 + fh of the row's scale word, SB0 = 0 or 2 by stage parity).
-#define MXQ_GEMM_READ(BUF, I, FA, FB, SA, SB, SB0)                                            \
-  do {                                                                                        \
-    FA[I][0] = lds_read16((BUF) + a_off[I] + c0);                                             \
-    FA[I][1] = lds_read16((BUF) + a_off[I] + c1);                                             \
-    FB[I][0] = lds_read16((BUF) + b_off[I] + c0);                                             \
-    FB[I][1] = lds_read16((BUF) + b_off[I] + c1);                                             \
-    SA[I] = lds_read1((BUF) + 2 * kSlice + (uint32_t)((wm * 128 + (I) * 32 + fr) * 4 + (SB0) + fh)); \
-    SB[I] = lds_read1((BUF) + 2 * kSlice + kScaleBytes +                                     \
-                      (uint32_t)((wn * 128 + (I) * 32 + fr) * 4 + (SB0) + fh));               \
-  } while (0)
-
-// Wait for this lane's fragment reads and make their registers visible as
-// written here (the compiler cannot see inside the reads).
-#define MXQ_GEMM_READ_WAIT(FA, FB, SA, SB)                                                    \
-  asm volatile("s_waitcnt lgkmcnt(0)"                                                         \
-               : "+v"(FA[0][0]), "+v"(FA[0][1]), "+v"(FA[1][0]), "+v"(FA[1][1]),             \
-                 "+v"(FA[2][0]), "+v"(FA[2][1]), "+v"(FA[3][0]), "+v"(FA[3][1]),             \
-                 "+v"(FB[0][0]), "+v"(FB[0][1]), "+v"(FB[1][0]), "+v"(FB[1][1]),             \
-                 "+v"(FB[2][0]), "+v"(FB[2][1]), "+v"(FB[3][0]), "+v"(FB[3][1]),             \
-                 "+v"(SA[0]), "+v"(SA[1]), "+v"(SA[2]), "+v"(SA[3]), "+v"(SB[0]),            \
-                 "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3]))
-
-// The 4 matrix instructions of A tile I of one stage, then an empty statement
-// taking their accumulators as inputs: it keeps them ahead of the volatile
-// LDS reads that follow (they touch no memory, so the compiler would
-// otherwise move them freely).
-#define MXQ_GEMM_MFMA_ROW(I, FA, FB, SA, SB)                                                  \
-  do {                                                                                        \
-    const v8i va = {FA[I][0].x, FA[I][0].y, FA[I][0].z, FA[I][0].w,                           \
-                    FA[I][1].x, FA[I][1].y, FA[I][1].z, FA[I][1].w};                          \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
-      const v8i vb = {FB[j][0].x, FB[j][0].y, FB[j][0].z, FB[j][0].w,                         \
-                      FB[j][1].x, FB[j][1].y, FB[j][1].z, FB[j][1].w};                        \
-      acc[I][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[I][j], 0, 0, 0, \
-                                                                  (int)SA[I], 0, (int)SB[j]); \
-    }                                                                                         \
-    asm volatile("" ::"a"(acc[I][0]), "a"(acc[I][1]), "a"(acc[I][2]), "a"(acc[I][3]));        \
-  } while (0)
+// LDS layouts.  Copy stage j lives in buffer j & 1: A rows at [0, kSlice), B
+// rows at [kSlice, kBuf), row r at r * 128.  Logical 16-byte chunk c of row r
+// is stored at physical chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 3):
+// the 16 rows one fragment read touches land on 16 different bank groups.
+// Scale group G (copy stages 4G .. 4G+3) lives in set G mod 3: the record of
+// A row r at r * 16, of B row r at 4 KiB + r * 16; it holds scale dwords
+// 4G .. 4G+3 of the row (blocks 16G .. 16G+15), dword d at position
+// (d + (r >> 3)) & 3.
 
 __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kBuf];  // 132 KiB of 160
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   const uint32_t base = (uint32_t)(size_t)(MXQ_LDS uint8_t*)smem;
 
   const int lane = threadIdx.x & 63;
@@ -183,20 +138,32 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;  // this wave's 128 x 128 quarter
   const int fr = lane & 31;                 // fragment row / column within a 32-tile
   const int fh = lane >> 5;                 // which 16-byte half of each k-block
-  const int KB = g.K >> 5;
-  const int nstages = g.K / kStageK;
+  const int K = g.K;
+  const int KB = K >> 5;
+  const int nstages = K / kCopyK;
   const int ntiles = g.tiles_m * g.tiles_n;
 
-  // This lane's fragment rows inside a buffer.  Every such row is fr modulo 8,
-  // so logical chunk c sits at physical chunk c ^ ((fr >> 1) & 3).
-  uint32_t a_off[4], b_off[4];
+  // Read side.  Every fragment row of this lane is fr modulo 32, so its
+  // swizzle is that of fr and its scale-record rotation is (fr >> 3) & 3.
+  const int fz = (fr & 7) ^ ((fr >> 3) & 3);
+  const int srot = (fr >> 3) & 3;
+  uint32_t a_off[4], b_off[4], as_off[4], bs_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kRowBytes);
-    b_off[i] = kSlice + (uint32_t)((wn * 128 + i * 32 + fr) * kRowBytes);
+    a_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kCopyK);
+    b_off[i] = kSlice + (uint32_t)((wn * 128 + i * 32 + fr) * kCopyK);
+    as_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kScaleRec);
+    bs_off[i] = kTile * kScaleRec + (uint32_t)((wn * 128 + i * 32 + fr) * kScaleRec);
   }
-  const uint32_t c0 = (uint32_t)((fh ^ ((fr >> 1) & 3)) << 4);
-  const uint32_t c1 = (uint32_t)(((2 + fh) ^ ((fr >> 1) & 3)) << 4);
+  // chunk offset of sub-stage half v (of a copy stage), k-block h
+  uint32_t coff[2][2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) coff[v][h] = (uint32_t)(((4 * v + 2 * h + fh) ^ fz) << 4);
+
+  // Copy side: lane -> (row within an 8-row group, physical chunk).
+  const int crow = lane >> 3, cphys = lane & 7;
 
   // Tiles of this workgroup.  Workgroup bid runs on XCD bid % 8: when the
   // counts allow, XCD x takes the contiguous range [x T/8, (x+1) T/8) of the
@@ -217,18 +184,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
     int tm, tn;
     tile_coords(t, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-
-    // global sources of this wave's DMA rows (ragged tiles: clamped rows)
-    const uint8_t* arow[4];
-    const uint8_t* brow[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = wave * 64 + q * 16 + (lane >> 2);
-      arow[q] = g.a + min(m0 + r, g.M - 1) * (int64_t)g.K;
-      brow[q] = g.b + min(n0 + r, g.N - 1) * (int64_t)g.K;
-    }
-    const uint8_t* ascl = g.as + min(m0 + wave * 64 + lane, g.M - 1) * (int64_t)KB;
-    const uint8_t* bscl = g.bs + min(n0 + wave * 64 + lane, g.N - 1) * (int64_t)KB;
+    const uint32_t rows_a = (uint32_t)min((int64_t)kTile, g.M - m0);
+    const uint32_t rows_b = (uint32_t)min((int64_t)kTile, g.N - n0);
+    const rsrc_t ra = make_rsrc(g.a + m0 * K, rows_a * (uint32_t)K);
+    const rsrc_t rb = make_rsrc(g.b + n0 * K, rows_b * (uint32_t)K);
+    const rsrc_t rsa = make_rsrc(g.as + m0 * KB, rows_a * (uint32_t)KB);
+    const rsrc_t rsb = make_rsrc(g.bs + n0 * KB, rows_b * (uint32_t)KB);
 
     v16f acc[4][4];
 #pragma unroll
@@ -238,40 +199,161 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Prologue: stages 0..3 in flight; wait for stage 0 (older vector-memory
-    // operations, such as the previous tile's C stores, retire first).
-    __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
-    MXQ_GEMM_DMA(base, 0);
-    if (nstages > 1) MXQ_GEMM_DMA(base + kBuf, kStageK);
-    if (nstages > 2) MXQ_GEMM_DMA(base + 2 * kBuf, 2 * kStageK);
-    if (nstages > 3) MXQ_GEMM_DMA(base + 3 * kBuf, 3 * kStageK);
-    if (nstages > 3) wait_vmcnt<3 * kDmaOps>();
-    else if (nstages > 2) wait_vmcnt<2 * kDmaOps>();
-    else if (nstages > 1) wait_vmcnt<kDmaOps>();
-    else wait_vmcnt<0>();
+// Copy instruction D (0..15) of copy stage J: operand A for D < 8, B
+// otherwise; 8 rows (64 wave + 8 (D % 8) + lane / 8) x 128 bytes, lane l
+// filling physical chunk l % 8 with the logical chunk that belongs there.
+#define MXQ_GEMM_DATA_OP(J, D)                                                                \
+    do {                                                                                      \
+      const int t_ = (D) & 7;                                                                 \
+      const int rl_ = wave * 64 + t_ * 8 + crow;                                              \
+      const int c_ = cphys ^ crow ^ (t_ & 3);                                                 \
+      const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)K + (uint32_t)((J) * kCopyK + c_ * 16); \
+      const uint32_t dst_ = base + (uint32_t)(((J) & 1) * kBuf) + ((D) >= 8 ? kSlice : 0) +   \
+                            (uint32_t)((wave * 64 + t_ * 8) * kCopyK);                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((D) >= 8 ? rb : ra,                            \
+                                               (MXQ_LDS void*)(size_t)dst_, 16, (int)voff_, 0, \
+                                               0, 0);                                         \
+    } while (0)
+
+// Scale copy KOP (0..7) of group GRP: operand A for KOP < 4, B otherwise; 16
+// rows (64 wave + 16 (KOP % 4) + lane / 4), lane l filling position l % 4 of
+// its row's record.  Dwords past the row's end are clamped to its last one
+// (never read).
+#define MXQ_GEMM_SCALE_OP(GRP, KOP)                                                           \
+    do {                                                                                      \
+      const int k_ = (KOP), t_ = k_ & 3;                                                      \
+      const int rl_ = wave * 64 + t_ * 16 + (lane >> 2);                                      \
+      const int q_ = ((lane & 3) - ((2 * t_ + (lane >> 5)) & 3)) & 3;                         \
+      const int gq_ = min(4 * (GRP) + q_, KB / 4 - 1);                                        \
+      const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)KB + (uint32_t)(4 * gq_);              \
+      const uint32_t dst_ = base + kScaleBase + (uint32_t)(mod3(GRP) * kScaleSet) +           \
+                            (k_ >= 4 ? kTile * kScaleRec : 0) +                               \
+                            (uint32_t)((wave * 64 + t_ * 16) * kScaleRec);                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_ >= 4 ? rsb : rsa,                           \
+                                               (MXQ_LDS void*)(size_t)dst_, 4, (int)voff_, 0, \
+                                               0, 0);                                         \
+    } while (0)
+
+// Copy instruction X (0..17) of stage J: its 16 data copies, then scale
+// copies 2 (J % 4) and 2 (J % 4) + 1 of group J / 4 + 1 (issued once group
+// J / 4 - 2, the set's previous tenant, is no longer read; landed long before
+// stage 4 (J / 4 + 1) is read).
+#define MXQ_GEMM_OP(J, X)                                                                     \
+    do {                                                                                      \
+      if ((X) < 16) MXQ_GEMM_DATA_OP(J, X);                                                   \
+      else MXQ_GEMM_SCALE_OP(((J) >> 2) + 1, 2 * ((J) & 3) + (X) - 16);                       \
+    } while (0)
+
+// Fragment read R (0..23) of sub-stage U into NA/NB (operand chunks) and
+// NSA/NSB (the scale dword of the sub-stage's copy stage).
+#define MXQ_GEMM_READ(U, R, NA, NB, NSA, NSB)                                                 \
+    do {                                                                                      \
+      const int ur_ = (U);                                                                    \
+      if ((R) < 16) {                                                                         \
+        const int ii_ = (R) >> 2, h_ = ((R) >> 1) & 1;                                        \
+        const uint32_t b_ = base + (uint32_t)(((ur_ >> 1) & 1) * kBuf) + coff[ur_ & 1][h_];   \
+        if ((R) & 1) NB[ii_][h_] = lds_read16(b_ + b_off[ii_]);                               \
+        else NA[ii_][h_] = lds_read16(b_ + a_off[ii_]);                                       \
+      } else {                                                                                \
+        const int jr_ = ur_ >> 1;                                                             \
+        const uint32_t s_ = base + kScaleBase + (uint32_t)(mod3(jr_ >> 2) * kScaleSet) +      \
+                            (uint32_t)((((jr_ & 3) + srot) & 3) * 4);                         \
+        if ((R) < 20) NSA[(R) - 16] = lds_read4(s_ + as_off[(R) - 16]);                       \
+        else NSB[(R) - 20] = lds_read4(s_ + bs_off[(R) - 20]);                                \
+      }                                                                                       \
+    } while (0)
+
+// Wait for this lane's fragment reads and make their registers visible as
+// written here (the compiler cannot see inside the reads); then move each
+// lane's scale byte of sub-stage U (byte 2 (U % 2) + fh of the dword) to byte 0.
+#define MXQ_GEMM_READ_DONE(U, NA, NB, NSA, NSB)                                               \
+    do {                                                                                      \
+      asm volatile("s_waitcnt lgkmcnt(0)"                                                     \
+                   : "+v"(NA[0][0]), "+v"(NA[0][1]), "+v"(NA[1][0]), "+v"(NA[1][1]),         \
+                     "+v"(NA[2][0]), "+v"(NA[2][1]), "+v"(NA[3][0]), "+v"(NA[3][1]),         \
+                     "+v"(NB[0][0]), "+v"(NB[0][1]), "+v"(NB[1][0]), "+v"(NB[1][1]),         \
+                     "+v"(NB[2][0]), "+v"(NB[2][1]), "+v"(NB[3][0]), "+v"(NB[3][1]),         \
+                     "+v"(NSA[0]), "+v"(NSA[1]), "+v"(NSA[2]), "+v"(NSA[3]), "+v"(NSB[0]),   \
+                     "+v"(NSB[1]), "+v"(NSB[2]), "+v"(NSB[3]));                              \
+      const uint32_t sh_ = 8 * fh + 16 * ((U) & 1);                                           \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
+        NSA[i_] >>= sh_;                                                                      \
+        NSB[i_] >>= sh_;                                                                      \
+      }                                                                                       \
+    } while (0)
+
+    // Prologue: stages 0 and 1 (and scale groups 0 and 1's first copies)
+    // out, wait for stage 0, read sub-stage 0.
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's LDS
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(0, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) MXQ_GEMM_SCALE_OP(0, k);
+    if (nstages > 1) {
+#pragma unroll
+      for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(1, x);
+      wait_vmcnt<kCopyOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();
 
-    // Stage s: read this stage's fragments, issue its 16 matrix instructions,
-    // wait for stage s + 1 to land in every wave; after that barrier every wave
-    // is done reading this stage's buffer, which then takes stage s + 4.
-    for (int s = 0; s < nstages; ++s) {
-      const uint32_t buf = base + (uint32_t)((s & 3) * kBuf);
-      v4i fa[4][2], fb[4][2];
-      uint32_t sa[4], sb[4];
+    v4i xa[4][2], xb[4][2], ya[4][2], yb[4][2];
+    uint32_t xsa[4], xsb[4], ysa[4], ysb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) MXQ_GEMM_READ(buf, i, fa, fb, sa, sb, (2 * s) & 3);
-      MXQ_GEMM_READ_WAIT(fa, fb, sa, sb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) MXQ_GEMM_MFMA_ROW(i, fa, fb, sa, sb);
-      if (s + 1 < nstages) {
-        // stages s+1 .. s+3 were issued; wait for s+1 (later ones may stay out)
-        if (s + 3 < nstages) wait_vmcnt<2 * kDmaOps>();
-        else if (s + 2 < nstages) wait_vmcnt<kDmaOps>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // also: every wave is done reading buffer s & 3
-        if (s + 4 < nstages) MXQ_GEMM_DMA(buf, (s + 4) * kStageK);
-      }
+    for (int r = 0; r < 24; ++r) MXQ_GEMM_READ(0, r, xa, xb, xsa, xsb);
+    MXQ_GEMM_READ_DONE(0, xa, xb, xsa, xsb);
+
+// Sub-stage U = 2j + ODD: its 16 matrix instructions from CA/CB/CSA/CSB, with
+// the reads of sub-stage U + 1 into NA/NB/NSA/NSB spread over the first 12
+// and, in odd sub-stages, the copies of stage j + 2 over all 16 (buffer j % 2
+// is free: every wave passed the barrier after reading its last sub-stage).
+// Even sub-stages end by waiting for stage j + 1 and a barrier.  The empty
+// statement after each instruction keeps it ahead of the memory instructions
+// that follow (it touches no memory, so the compiler would move it freely).
+#define MXQ_GEMM_SUBSTAGE(U, ODD, CA, CB, CSA, CSB, NA, NB, NSA, NSB)                          \
+    do {                                                                                      \
+      const int u_ = (U);                                                                     \
+      const int j_ = u_ >> 1;                                                                 \
+      const bool rd_ = (ODD) ? (j_ + 1 < nstages) : true;                                     \
+      const bool cp_ = (ODD) && (j_ + 2 < nstages);                                           \
+      _Pragma("unroll") for (int m = 0; m < 16; ++m) {                                        \
+        if (cp_) {                                                                            \
+          MXQ_GEMM_OP(j_ + 2, m);                                                             \
+          if (m < 2) MXQ_GEMM_OP(j_ + 2, 16 + m);                                             \
+        }                                                                                     \
+        if (m < 12 && rd_) {                                                                  \
+          MXQ_GEMM_READ(u_ + 1, 2 * m, NA, NB, NSA, NSB);                                     \
+          MXQ_GEMM_READ(u_ + 1, 2 * m + 1, NA, NB, NSA, NSB);                                 \
+        }                                                                                     \
+        const int i = m >> 2, j = m & 3;                                                      \
+        const v8i va = {CA[i][0].x, CA[i][0].y, CA[i][0].z, CA[i][0].w,                       \
+                        CA[i][1].x, CA[i][1].y, CA[i][1].z, CA[i][1].w};                      \
+        const v8i vb = {CB[j][0].x, CB[j][0].y, CB[j][0].z, CB[j][0].w,                       \
+                        CB[j][1].x, CB[j][1].y, CB[j][1].z, CB[j][1].w};                      \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[i][j], 0, 0, 0, \
+                                                                    (int)CSA[i], 0, (int)CSB[j]); \
+        asm volatile("" ::"a"(acc[i][j]));                                                    \
+      }                                                                                       \
+      if (rd_) MXQ_GEMM_READ_DONE(u_ + 1, NA, NB, NSA, NSB);                                  \
+      if (!(ODD) && j_ + 1 < nstages) {                                                       \
+        wait_vmcnt<0>();                                                                      \
+        __builtin_amdgcn_s_barrier();                                                         \
+        asm volatile("" ::: "memory");                                                        \
+      }                                                                                       \
+    } while (0)
+
+    for (int u = 0; u < 2 * nstages; u += 2) {
+      MXQ_GEMM_SUBSTAGE(u, 0, xa, xb, xsa, xsb, ya, yb, ysa, ysb);
+      MXQ_GEMM_SUBSTAGE(u + 1, 1, ya, yb, ysa, ysb, xa, xb, xsa, xsb);
     }
+#undef MXQ_GEMM_SUBSTAGE
+#undef MXQ_GEMM_READ_DONE
+#undef MXQ_GEMM_READ
+#undef MXQ_GEMM_OP
+#undef MXQ_GEMM_SCALE_OP
+#undef MXQ_GEMM_DATA_OP
 
     // epilogue: lane l, register r -> row (r%4) + 8(r/4) + 4(l/32), column l%32
     const int64_t row0 = m0 + wm * 128 + 4 * fh, col0 = n0 + wn * 128 + fr;
@@ -281,9 +363,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float* crow = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
+          float* crow_p = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) crow[j * 32] = acc[i][j][r];
+          for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(acc[i][j][r], crow_p + j * 32);
         }
     } else {
 #pragma unroll
