@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
+FP8_DENSE_PEAK = 5.0e15          # MI355X dense fp8 matrix peak, FLOP/s
 HEADLINE = 3                     # workload number of the headline line
 METRIC = "MXNorm fwd HBM GB/s (% of MI355X peak), hidden=4096, 16k rows bf16"
 KERNEL_SOURCES = ["mx_quantised_tensor_amd/csrc/mxnorm_kernels.hip",
@@ -269,6 +270,43 @@ def main():
             extras[key + "_us_per_call"] = round(gt / nb * 1e6, 3)
             extras[key + "_algorithmic_GBps"] = round(bb / (gt / nb) / 1e9, 1)
         del bsets
+        torch.cuda.empty_cache()
+
+        # MXNormLinear on the headline matrix: the gain folded into a square
+        # weight (hidden x hidden, cast once), then per step mxnorm_fwd with no
+        # gain into MXFP8 + the MXFP8 matmul (fp32 out).  The matmul alone is
+        # priced against the fp8 dense matrix peak.
+        wbits = W.linear_weight(hidden, hidden, HEADLINE)
+        wdev = torch.from_numpy(wbits.view(np.int16)).to(dev)
+        wc = torch.empty((hidden, hidden), dtype=torch.uint8, device=dev)
+        wsc = torch.empty((hidden, hidden // 32), dtype=torch.uint8, device=dev)
+        mxq.mx_quant_gain(wdev.view(torch.bfloat16), gb_dev.view(torch.bfloat16), codes=wc,
+                          scales=wsc)
+        lsets = []
+        for i in range(2):
+            lsets.append(dict(x=torch.from_numpy(xb.view(np.int16)).to(dev),
+                              xc=torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
+                              xs=torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev),
+                              out=torch.empty((rows, hidden), dtype=torch.float32, device=dev)))
+        for s in lsets:
+            mxq.mxnorm_fwd(s["x"].view(torch.bfloat16), None, p=2, codes=s["xc"], scales=s["xs"])
+        mm = [lambda s=s: L.mx_matmul(s["xc"].data_ptr(), s["xs"].data_ptr(), wc.data_ptr(),
+                                      wsc.data_ptr(), rows, hidden, hidden, s["out"].data_ptr(),
+                                      sp) for s in lsets]
+        nm = max(20, args.steps // 20)
+        _, gt = time_region(mm, nm, None)
+        flops = 2.0 * rows * hidden * hidden
+        extras["mx_matmul_shape"] = [rows, hidden, hidden]
+        extras["mx_matmul_us_per_call"] = round(gt / nm * 1e6, 3)
+        extras["mx_matmul_TFLOPs"] = round(flops / (gt / nm) / 1e12, 1)
+        extras["mx_matmul_frac_of_fp8_dense_peak"] = round(flops / (gt / nm) / FP8_DENSE_PEAK, 4)
+        lin = [lambda s=s: L.mxnorm_linear_fwd(s["x"].data_ptr(), rows, hidden, 2, C_P2,
+                                               wc.data_ptr(), wsc.data_ptr(), hidden,
+                                               s["xc"].data_ptr(), s["xs"].data_ptr(), None,
+                                               s["out"].data_ptr(), sp) for s in lsets]
+        _, gt = time_region(lin, nm, None)
+        extras["mxnorm_linear_fwd_us_per_call"] = round(gt / nm * 1e6, 3)
+        del lsets, wdev, wc, wsc
         torch.cuda.empty_cache()
 
         # Context: a plain device-to-device copy (torch's copy kernel) of 1 GiB,

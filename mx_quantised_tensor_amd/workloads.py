@@ -117,3 +117,11 @@ def random_rows(rows: int, hidden: int, seed: int, scale_spread: float = 0.0):
         u = rng.uniform(-scale_spread / 2, scale_spread / 2, size=(rows, 1))
         x *= np.exp2(u).astype(np.float32)
     return x
+
+
+def linear_weight(out_features: int, hidden: int, seed: int):
+    """Weight of the linear layer after the norm: N(0, 1/hidden) (fan-in
+    scaling), bf16 bits, [out_features, hidden].  Own stream (seed + 104729)."""
+    rng = np.random.default_rng(seed + 104729)
+    w = rng.standard_normal((out_features, hidden), dtype=np.float32)
+    return to_bf16_bits(w * np.float32(1.0 / np.sqrt(hidden)))
