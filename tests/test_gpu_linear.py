@@ -52,8 +52,12 @@ def _check(ac, as_, bc, bs, what, sample=None, seed=0):
     P.assert_matmul_close(c[mn[:, 0], mn[:, 1]], want, A, B, mn, what)
 
 
+# K spans 1 .. 16 copy stages of 128, partial scale groups (640, 1152: the
+# last group of 4 copy stages is short) and all three rotating scale sets;
+# M, N ragged and below, at and above one 256 x 256 tile.
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 128, 512), (100, 70, 256),
-                                   (1, 1, 128), (33, 257, 1024), (130, 384, 2048)])
+                                   (1, 1, 128), (33, 257, 1024), (130, 384, 2048),
+                                   (300, 260, 640), (513, 1000, 1152), (600, 700, 1536)])
 def test_matmul_shapes(M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     ac, as_ = rand_mx(rng, M, K)
@@ -78,6 +82,15 @@ def test_matmul_headline_shape_sampled():
     ac, as_ = rand_mx(rng, 16384, 4096, 120, 132)
     bc, bs = rand_mx(rng, 4096, 4096, 120, 132)
     _check(ac, as_, bc, bs, "16384x4096x4096 sampled", sample=1500, seed=3)
+
+
+def test_matmul_many_tiles_sampled():
+    # 17 x 17 = 289 tiles: more tiles than persistent workgroups, and a count
+    # that is not a multiple of the 8 XCDs (the round-robin tile order)
+    rng = np.random.default_rng(15)
+    ac, as_ = rand_mx(rng, 4352, 256, 120, 132)
+    bc, bs = rand_mx(rng, 4352, 256, 120, 132)
+    _check(ac, as_, bc, bs, "4352x4352x256 sampled", sample=1500, seed=4)
 
 
 @pytest.mark.parametrize("elem", [0, 1])
