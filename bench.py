@@ -11,11 +11,14 @@ the current stream; one HIP event pair brackets the K timed steps.
 Printed: one JSON line with the achieved algorithmic HBM throughput (GB/s),
 a roofline object for the kernel, the CPU oracle timed on the host as a
 reference baseline, and context figures (the two-pass RMSNorm + MX cast
-baseline, the straight-through backward on the same matrix, the other
-workloads, a rotated 1 GiB device copy).
+baseline, the straight-through backward on the same matrix, MXNormLinear
+(the MXFP8 matmul on the same matrix times a 4096 x 4096 folded weight), the
+other workloads, a rotated 1 GiB device copy).
 
 `python bench.py --counters` only runs the headline kernel and a 256 MiB
-device copy (the calibration for HBM byte counters) for rocprofv3 --pmc.
+device copy (the calibration for HBM byte counters) for rocprofv3 --pmc;
+`python bench.py --counters-matmul` only runs the 16384 x 4096 x 4096 MXFP8
+matmul (5 launches), for the matrix kernel's counters.
 """
 import argparse
 import hashlib
@@ -94,6 +97,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--counters", action="store_true",
                     help="run only the headline kernel and a calibration copy (for --pmc)")
+    ap.add_argument("--counters-matmul", action="store_true",
+                    help="run only the 16384x4096x4096 MXFP8 matmul, 5 times (for --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -194,6 +199,18 @@ def main():
     w = W.WORKLOADS[HEADLINE]
     xb, gb = W.workload_inputs(HEADLINE)
     rows, hidden = xb.shape
+    if args.counters_matmul:
+        xt = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        xc, xs = mxq.mxnorm_fwd(xt, None, p=2)[:2]
+        wt = torch.from_numpy(W.linear_weight(hidden, hidden, HEADLINE).view(np.int16)).to(dev)
+        gt_ = torch.from_numpy(gb.view(np.int16)).to(dev)
+        wc, wsc = mxq.mx_quant_gain(wt.view(torch.bfloat16), gt_.view(torch.bfloat16))
+        out = torch.empty((rows, hidden), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            mxq.mx_matmul(xc, xs, wc, wsc, c=out)
+        torch.cuda.synchronize()
+        print("counters run: 5 x mx_matmul %dx%dx%d" % (rows, hidden, hidden))
+        return
     g, sets = device_sets(xb, gb, w.elem, args.buffers)
     calls = mxnorm_calls(sets, g, rows, hidden, 2, w.elem)
     nbytes = algorithmic_bytes(rows, hidden, w.elem)
