@@ -243,6 +243,16 @@ def main():
               "kernel_source_hash": kernel_hash()}
 
     if not args.no_extras:
+        # the same workload without a gain (MXNormLinear mode)
+        ng_calls = [lambda s=s: L.mxnorm_fwd(s["x"].data_ptr(), None, rows, hidden, 2, 0.0, w.elem,
+                                             s["codes"].data_ptr(), s["scales"].data_ptr(),
+                                             s["rrms"].data_ptr(), sp) for s in sets]
+        nng = max(30, args.steps // 4)
+        _, gng = time_region(ng_calls, nng, None)
+        extras["headline_no_gain_us_per_call"] = round(gng / nng * 1e6, 3)
+        extras["headline_no_gain_algorithmic_GBps"] = round(
+            algorithmic_bytes(rows, hidden, w.elem, gamma=False) / (gng / nng) / 1e9, 1)
+        del ng_calls
         # two-pass baseline on the same workload
         del sets, calls
         torch.cuda.empty_cache()
@@ -372,16 +382,38 @@ def main():
     if not args.no_cpu:
         import oracle as O
         O.lib()
-        reps = []
-        for _ in range(2):
-            t0 = time.perf_counter()
-            O.mxnorm_fwd(xb, gb, 2, C_P2, w.elem)
-            reps.append(time.perf_counter() - t0)
-        t = min(reps)
+        threads = O.max_threads()
+
+        def oracle_runs(n):
+            reps = []
+            for _ in range(n):
+                t0 = time.perf_counter()
+                O.mxnorm_fwd(xb, gb, 2, C_P2, w.elem)
+                reps.append(time.perf_counter() - t0)
+            return sorted(reps)[len(reps) // 2]
+
+        t = oracle_runs(3)
         cpu = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s",
-               "cores": O.max_threads(), "kind": "oracle",
-               "sample": "the full 16384x4096 headline matrix, best of 2 runs "
-                         "(%.2f s each), OpenMP over rows" % t}
+               "cores": threads, "kind": "oracle",
+               "sample": "the full 16384x4096 headline matrix, median of 3 runs "
+                         "(%.2f s), OpenMP over rows on %d threads" % (t, threads)}
+        O.set_threads(1)
+        t1 = oracle_runs(3)
+        O.set_threads(threads)
+        extras["cpu_oracle_single_thread_GBps"] = round(nbytes / t1 / 1e9, 4)
+        extras["cpu_oracle_single_thread_s"] = round(t1, 3)
+        extras["cpu_oracle_rows_per_s"] = round(rows / t, 1)
+        extras["host_nproc"] = os.cpu_count()
+        model = None
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+        extras["host_cpu_model"] = model
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,

@@ -74,6 +74,8 @@ def lib():
         L.mxo_encode_array.argtypes = [C.POINTER(C.c_double), i64, C.c_int, u8p]
         L.mxo_max_threads.restype = C.c_int
         L.mxo_max_threads.argtypes = []
+        L.mxo_set_threads.restype = None
+        L.mxo_set_threads.argtypes = [C.c_int]
         f64p = C.POINTER(C.c_double)
         L.mxo_mx_quant_gain.restype = C.c_int
         L.mxo_mx_quant_gain.argtypes = [u16p, u16p, i64, i64, C.c_int, u8p, u8p]
@@ -244,6 +246,11 @@ def rmsnorm_mxquant_fwd(x, gamma, eps, elem):
 
 def max_threads():
     return lib().mxo_max_threads()
+
+
+def set_threads(n):
+    """Thread count of the oracle's OpenMP loops (for timing the CPU baseline)."""
+    lib().mxo_set_threads(int(n))
 
 
 def mxnorm_bwd(x, dy, gamma, rho):

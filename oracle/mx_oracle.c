@@ -765,3 +765,14 @@ int mxo_max_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops (timing of the CPU baseline only). */
+void mxo_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
