@@ -210,6 +210,7 @@ def _mm(a=A16, as_=A16, b=A16, bs=A16, M=128, N=128, K=256, c=A16):
 
 def test_matmul_argument_checks():
     assert _mm(K=96) == EUNSUP          # a multiple of 32 but not of 128
+    assert _mm(K=131072 + 128) == EUNSUP  # beyond the largest K
     assert _mm(K=100) == EINVAL
     assert _mm(K=0) == EINVAL
     assert _mm(M=-1) == EINVAL
