@@ -314,12 +314,13 @@ def main():
             lsets.append(dict(x=torch.from_numpy(xb.view(np.int16)).to(dev),
                               xc=torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
                               xs=torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev),
-                              out=torch.empty((rows, hidden), dtype=torch.float32, device=dev)))
+                              out=torch.empty((rows, hidden), dtype=torch.float32, device=dev),
+                              outh=torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)))
         for s in lsets:
             mxq.mxnorm_fwd(s["x"].view(torch.bfloat16), None, p=2, codes=s["xc"], scales=s["xs"])
         mm = [lambda s=s: L.mx_matmul(s["xc"].data_ptr(), s["xs"].data_ptr(), wc.data_ptr(),
                                       wsc.data_ptr(), rows, hidden, hidden, s["out"].data_ptr(),
-                                      sp) for s in lsets]
+                                      mxq.OUT_F32, sp) for s in lsets]
         nm = max(20, args.steps // 20)
         _, gt = time_region(mm, nm, None)
         flops = 2.0 * rows * hidden * hidden
@@ -330,9 +331,17 @@ def main():
         lin = [lambda s=s: L.mxnorm_linear_fwd(s["x"].data_ptr(), rows, hidden, 2, C_P2,
                                                wc.data_ptr(), wsc.data_ptr(), hidden,
                                                s["xc"].data_ptr(), s["xs"].data_ptr(), None,
-                                               s["out"].data_ptr(), sp) for s in lsets]
+                                               s["out"].data_ptr(), mxq.OUT_F32, sp)
+               for s in lsets]
         _, gt = time_region(lin, nm, None)
         extras["mxnorm_linear_fwd_us_per_call"] = round(gt / nm * 1e6, 3)
+        # the same product with a bf16 output (the fp32 result rounded)
+        mmh = [lambda s=s: L.mx_matmul(s["xc"].data_ptr(), s["xs"].data_ptr(), wc.data_ptr(),
+                                       wsc.data_ptr(), rows, hidden, hidden, s["outh"].data_ptr(),
+                                       mxq.OUT_BF16, sp) for s in lsets]
+        _, gt = time_region(mmh, nm, None)
+        extras["mx_matmul_bf16_out_us_per_call"] = round(gt / nm * 1e6, 3)
+        extras["mx_matmul_bf16_out_TFLOPs"] = round(flops / (gt / nm) / 1e12, 1)
         del lsets, wdev, wc, wsc
         torch.cuda.empty_cache()
 

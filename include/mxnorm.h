@@ -71,6 +71,12 @@ typedef enum {
     MXQ_SRC_ABSMAX = 1      /* the exact block absmax max_i |x_i| */
 } mxq_source;
 
+/* Element type of a matrix-product output. */
+typedef enum {
+    MXQ_OUT_F32 = 0,        /* fp32 */
+    MXQ_OUT_BF16 = 1        /* bf16: the fp32 result rounded to nearest even */
+} mxq_out;
+
 #define MXQ_BLOCK 32
 #define MXQ_MAX_HIDDEN 32768
 
@@ -186,7 +192,8 @@ mxq_status mx_quant_gain(const void *w, const void *gamma, int64_t rows, int64_t
  *   a_codes  : device [M, K] E4M3, 16-byte aligned;  a_scales : [M, K/32]
  *   b_codes  : device [N, K] E4M3, 16-byte aligned;  b_scales : [N, K/32]
  *              (scales 4-byte aligned)
- *   c        : device fp32 [M, N] out
+ *   c        : device [M, N] out, fp32 or bf16 (c_type, mxq_out), 4-byte
+ *              aligned; bf16 is the fp32 result rounded to nearest even
  * K must be a multiple of 128 (MXQ_EUNSUPPORTED otherwise; MXQ_EINVAL if not
  * a multiple of 32).  A 0xFF scale makes the outputs that use its block NaN.
  * Numerics: each 64-element slice of k is summed by the matrix unit, which
@@ -195,8 +202,8 @@ mxq_status mx_quant_gain(const void *w, const void *gamma, int64_t rows, int64_t
  * accumulated in fp32.
  */
 mxq_status mx_matmul(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
-                     const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, float *c,
-                     mxq_stream_t stream);
+                     const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *c,
+                     mxq_out c_type, mxq_stream_t stream);
 
 /*
  * mxnorm_linear_fwd -- the MXNormLinear forward of [P1] §2: mxnorm_fwd with no
@@ -206,12 +213,14 @@ mxq_status mx_matmul(const uint8_t *a_codes, const uint8_t *a_scales, const uint
  *   x        : device bf16 [rows, hidden]; hidden a multiple of 128
  *   w_codes, w_scales : device [out_features, hidden], [out_features, hidden/32]
  *   x_codes, x_scales : device scratch/outputs [rows, hidden], [rows, hidden/32]
- *   rrms     : device fp32 [rows] or NULL;  out : device fp32 [rows, out_features]
+ *   rrms     : device fp32 [rows] or NULL
+ *   out      : device [rows, out_features], fp32 or bf16 (out_type), as
+ *              mx_matmul's c
  */
 mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p, float c,
                              const uint8_t *w_codes, const uint8_t *w_scales,
                              int64_t out_features, uint8_t *x_codes, uint8_t *x_scales,
-                             float *rrms, float *out, mxq_stream_t stream);
+                             float *rrms, void *out, mxq_out out_type, mxq_stream_t stream);
 
 /*
  * mxnorm_bwd -- straight-through MXNorm backward ([P1] §2 "Implementacion",

@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
            "mxnorm_bwd", "mxnorm_bwd_workspace_bytes", "mxnorm_fwd_ex", "SRC_SCALES",
-           "SRC_ABSMAX", "mx_quant_gain", "mx_matmul", "mxnorm_linear_fwd",
+           "SRC_ABSMAX", "OUT_F32", "OUT_BF16", "mx_quant_gain", "mx_matmul", "mxnorm_linear_fwd",
            "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
            "library_path"]
 
@@ -26,6 +26,8 @@ E2M1 = 1
 BLOCK = 32
 SRC_SCALES = 0   # block magnitude = the E8M0 scale as a power of two (mxnorm_fwd)
 SRC_ABSMAX = 1   # block magnitude = the exact block absmax
+OUT_F32 = 0      # matrix-product output types
+OUT_BF16 = 1
 MAX_HIDDEN = 32768
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,9 +70,10 @@ def lib():
         L.mx_quant_gain.restype = i32
         L.mx_quant_gain.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
         L.mx_matmul.restype = i32
-        L.mx_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        L.mx_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
         L.mxnorm_linear_fwd.restype = i32
-        L.mxnorm_linear_fwd.argtypes = [vp, i64, i64, i32, f32, vp, vp, i64, vp, vp, vp, vp, vp]
+        L.mxnorm_linear_fwd.argtypes = [vp, i64, i64, i32, f32, vp, vp, i64, vp, vp, vp, vp, i32,
+                                        vp]
         L.mxnorm_fwd_ex.restype = i32
         L.mxnorm_fwd_ex.argtypes = [vp, vp, i64, i64, i32, f32, i32, i32, i32, vp, vp, vp, vp]
         L.mxnorm_default_c_for.restype = f32
@@ -263,8 +266,18 @@ def _u8_2d(t, name):
     return t
 
 
-def mx_matmul(a_codes, a_scales, b_codes, b_scales, c=None, stream=None):
-    """C = A B^T (fp32) for MXFP8 A [M, K] and B [N, K]."""
+def _out_type(t, name):
+    """mxq_out code of an output tensor's dtype (fp32 or bf16)."""
+    if t.dtype == torch.float32:
+        return OUT_F32
+    if t.dtype == torch.bfloat16:
+        return OUT_BF16
+    raise ValueError("%s must be float32 or bfloat16" % name)
+
+
+def mx_matmul(a_codes, a_scales, b_codes, b_scales, c=None, out_dtype=torch.float32, stream=None):
+    """C = A B^T for MXFP8 A [M, K] and B [N, K]; C fp32, or bf16 (the fp32
+    result rounded to nearest even) -- the dtype of c if given, else out_dtype."""
     a_codes, a_scales = _u8_2d(a_codes, "a_codes"), _u8_2d(a_scales, "a_scales")
     b_codes, b_scales = _u8_2d(b_codes, "b_codes"), _u8_2d(b_scales, "b_scales")
     M, K = a_codes.shape
@@ -273,16 +286,17 @@ def mx_matmul(a_codes, a_scales, b_codes, b_scales, c=None, stream=None):
             b_scales.shape != (N, K // BLOCK):
         raise ValueError("operand shapes do not agree")
     if c is None:
-        c = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+        c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
     _check(lib().mx_matmul(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
-                           _ptr(c), _stream(stream)), "mx_matmul")
+                           _ptr(c), _out_type(c, "c"), _stream(stream)), "mx_matmul")
     return c
 
 
 def mxnorm_linear_fwd(x, w_codes, w_scales, p=2, c=0.0, out=None, x_codes=None, x_scales=None,
-                      rrms=None, stream=None):
+                      rrms=None, out_dtype=torch.float32, stream=None):
     """MXNormLinear forward: mxnorm_fwd (no gain, E4M3) then mx_matmul with the
-    gain-folded MXFP8 weight -> (out fp32 [rows, out_features], x_codes, x_scales, rrms)."""
+    gain-folded MXFP8 weight -> (out [rows, out_features] fp32 or bf16, x_codes,
+    x_scales, rrms)."""
     x = _bf16_2d(x)
     rows, hidden = x.shape
     w_codes, w_scales = _u8_2d(w_codes, "w_codes"), _u8_2d(w_scales, "w_scales")
@@ -291,8 +305,8 @@ def mxnorm_linear_fwd(x, w_codes, w_scales, p=2, c=0.0, out=None, x_codes=None, 
     if rrms is None:
         rrms = torch.empty((rows,), dtype=torch.float32, device=x.device)
     if out is None:
-        out = torch.empty((rows, O), dtype=torch.float32, device=x.device)
+        out = torch.empty((rows, O), dtype=out_dtype, device=x.device)
     _check(lib().mxnorm_linear_fwd(_ptr(x), rows, hidden, p, c, _ptr(w_codes), _ptr(w_scales), O,
                                    _ptr(x_codes), _ptr(x_scales), _ptr(rrms), _ptr(out),
-                                   _stream(stream)), "mxnorm_linear_fwd")
+                                   _out_type(out, "out"), _stream(stream)), "mxnorm_linear_fwd")
     return out, x_codes, x_scales, rrms

@@ -29,9 +29,10 @@ hipError_t launch_mx_quant(const void* x, int64_t rows, int hidden, int elem, ui
 hipError_t launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int hidden, float eps,
                           void* y, float* rstd, void* stream);
 
-// MXFP8 x MXFP8 matrix product C[M, N] = A[M, K] B[N, K]^T (K % 128 == 0).
+// MXFP8 x MXFP8 matrix product C[M, N] = A[M, K] B[N, K]^T (K % 128 == 0),
+// C fp32, or bf16 (round to nearest even) when c_bf16.
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
-                          const uint8_t* bs, int64_t M, int64_t N, int K, float* c,
+                          const uint8_t* bs, int64_t M, int64_t N, int K, void* c, bool c_bf16,
                           void* stream);
 // MX cast of fl32(w * gamma) along rows of w (the gain folded into a weight).
 hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,

@@ -41,7 +41,9 @@
 // the buffer range and read as zero (their outputs are not stored).
 // Workgroups are persistent over tiles; tiles are taken in groups of 8 tile
 // rows for L2 locality, each XCD a contiguous range; C is written with
-// streaming (non-temporal) stores.
+// streaming (non-temporal) stores, as fp32 or as bf16 (round to nearest even;
+// adjacent lanes swap one value so that each lane stores two neighbouring
+// columns).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,6 +73,7 @@ constexpr int kMaxGroups = 256;                 // one persistent workgroup per 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 struct GemmArgs {
@@ -78,7 +81,7 @@ struct GemmArgs {
   const uint8_t* as;  // [M, K/32] E8M0
   const uint8_t* b;   // [N, K]
   const uint8_t* bs;  // [N, K/32]
-  float* c;           // [M, N]
+  void* c;            // [M, N] fp32 or bf16
   int64_t M, N;
   int K;
   int tiles_m, tiles_n;
@@ -129,6 +132,7 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // 4G .. 4G+3 of the row (blocks 16G .. 16G+15), dword d at position
 // (d + (r >> 3)) & 3.
 
+template <bool BF16>
 __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   const uint32_t base = (uint32_t)(size_t)(MXQ_LDS uint8_t*)smem;
@@ -357,8 +361,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 
     // epilogue: lane l, register r -> row (r%4) + 8(r/4) + 4(l/32), column l%32
     const int64_t row0 = m0 + wm * 128 + 4 * fh, col0 = n0 + wn * 128 + fr;
-    if (m0 + kTile <= g.M && n0 + kTile <= g.N) {
-      float* cb = g.c + row0 * g.N + col0;
+    const bool full = m0 + kTile <= g.M && n0 + kTile <= g.N;
+    if (!BF16 && full) {
+      float* cb = static_cast<float*>(g.c) + row0 * g.N + col0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -366,6 +371,28 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
           float* crow_p = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
 #pragma unroll
           for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(acc[i][j][r], crow_p + j * 32);
+        }
+    } else if (BF16 && full && (g.N & 1) == 0) {
+      // Registers r, r + 1 (r even) hold rows R, R + 1 of this lane's column.
+      // The even lane of a pair stores columns (2c, 2c + 1) of row R, the odd
+      // lane those of row R + 1: each sends its partner the value it lacks.
+      const bool odd = (lane & 1) != 0;
+      __bf16* cb = static_cast<__bf16*>(g.c) + (row0 + (odd ? 1 : 0)) * g.N + (col0 & ~(int64_t)1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          __bf16* crow_p = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+            const float send = odd ? v0 : v1;
+            const float recv = __int_as_float(__builtin_amdgcn_update_dpp(
+                0, __float_as_int(send), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, false));
+            const bf16x2 pk = {(__bf16)(odd ? recv : v0), (__bf16)(odd ? v1 : recv)};
+            __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, pk),
+                                        reinterpret_cast<uint32_t*>(crow_p + j * 32));
+          }
         }
     } else {
 #pragma unroll
@@ -376,7 +403,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t row = row0 + i * 32 + (r & 3) + 8 * (r >> 2);
-            if (row < g.M && col < g.N) g.c[row * g.N + col] = acc[i][j][r];
+            if (row < g.M && col < g.N) {
+              if (BF16) static_cast<__bf16*>(g.c)[row * g.N + col] = (__bf16)acc[i][j][r];
+              else static_cast<float*>(g.c)[row * g.N + col] = acc[i][j][r];
+            }
           }
         }
     }
@@ -386,7 +416,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 }  // namespace
 
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
-                          const uint8_t* bs, int64_t M, int64_t N, int K, float* c,
+                          const uint8_t* bs, int64_t M, int64_t N, int K, void* c, bool c_bf16,
                           void* stream) {
   GemmArgs g;
   g.a = a;
@@ -401,7 +431,11 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
   g.tiles_n = (int)((N + kTile - 1) / kTile);
   const int ntiles = g.tiles_m * g.tiles_n;
   const int groups = ntiles < kMaxGroups ? ntiles : kMaxGroups;
-  hipLaunchKernelGGL(k_mx_gemm, dim3(groups), dim3(kGemmThreads), 0, (hipStream_t)stream, g);
+  if (c_bf16)
+    hipLaunchKernelGGL(k_mx_gemm<true>, dim3(groups), dim3(kGemmThreads), 0, (hipStream_t)stream, g);
+  else
+    hipLaunchKernelGGL(k_mx_gemm<false>, dim3(groups), dim3(kGemmThreads), 0, (hipStream_t)stream,
+                       g);
   return hipGetLastError();
 }
 

@@ -152,9 +152,10 @@ mxq_status mx_quant_gain(const void* w, const void* gamma, int64_t rows, int64_t
 }
 
 mxq_status mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c,
-                     mxq_stream_t stream) {
+                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                     mxq_out c_type, mxq_stream_t stream) {
   if (M < 0 || N < 0 || K <= 0 || K % MXQ_BLOCK != 0) return MXQ_EINVAL;
+  if (c_type != MXQ_OUT_F32 && c_type != MXQ_OUT_BF16) return MXQ_EINVAL;
   if (K % kMatmulK != 0 || K > MXQ_MAX_HIDDEN * 4) return MXQ_EUNSUPPORTED;
   if (M > kMaxRows * 4 || N > kMaxRows * 4) return MXQ_EUNSUPPORTED;
   if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 31)) return MXQ_EUNSUPPORTED;
@@ -165,24 +166,26 @@ mxq_status mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, const uint
     return MXQ_EALIGN;
   (void)hipGetLastError();
   return status_of(mxq::launch_mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, (int)K, c,
-                                       stream));
+                                       c_type == MXQ_OUT_BF16, stream));
 }
 
 mxq_status mxnorm_linear_fwd(const void* x, int64_t rows, int64_t hidden, int p, float c,
                              const uint8_t* w_codes, const uint8_t* w_scales,
                              int64_t out_features, uint8_t* x_codes, uint8_t* x_scales,
-                             float* rrms, float* out, mxq_stream_t stream) {
+                             float* rrms, void* out, mxq_out out_type, mxq_stream_t stream) {
   mxq_status st = check_shape(rows, hidden, MXQ_E4M3);
   if (st != MXQ_OK) return st;
   if (p != 1 && p != 2) return MXQ_EINVAL;
   if (!(c >= 0.0f) || !isfinite(c)) return MXQ_EINVAL;
   if (out_features < 0) return MXQ_EINVAL;
+  if (out_type != MXQ_OUT_F32 && out_type != MXQ_OUT_BF16) return MXQ_EINVAL;
   if (hidden % kMatmulK != 0) return MXQ_EUNSUPPORTED;
   if (rows == 0 || out_features == 0) return MXQ_OK;
   st = mxnorm_common(x, nullptr, rows, hidden, p, c, MXQ_SRC_SCALES, 0, MXQ_E4M3, x_codes,
                      x_scales, rrms, stream);
   if (st != MXQ_OK) return st;
-  return mx_matmul(x_codes, x_scales, w_codes, w_scales, rows, out_features, hidden, out, stream);
+  return mx_matmul(x_codes, x_scales, w_codes, w_scales, rows, out_features, hidden, out,
+                   out_type, stream);
 }
 
 size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {

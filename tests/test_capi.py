@@ -204,8 +204,8 @@ def test_python_binding_rejects_bad_tensors_on_cpu():
         mxq.mx_quant(torch.zeros((4, 64), dtype=torch.float32))
 
 
-def _mm(a=A16, as_=A16, b=A16, bs=A16, M=128, N=128, K=256, c=A16):
-    return mxq.lib().mx_matmul(a, as_, b, bs, M, N, K, c, None)
+def _mm(a=A16, as_=A16, b=A16, bs=A16, M=128, N=128, K=256, c=A16, t=0):
+    return mxq.lib().mx_matmul(a, as_, b, bs, M, N, K, c, t, None)
 
 
 def test_matmul_argument_checks():
@@ -219,8 +219,13 @@ def test_matmul_argument_checks():
     assert _mm(a=MIS) == EALIGN
     assert _mm(bs=A16 + 2) == EALIGN
     assert _mm(c=A16 + 2) == EALIGN
+    assert _mm(c=A16 + 2, t=1) == EALIGN  # bf16 output: 4-byte aligned too
+    assert _mm(t=2) == EINVAL
+    assert _mm(t=-1) == EINVAL
     L = mxq.lib()
     assert L.mx_quant_gain(A16, None, 4, 64, 0, A16, A16, None) == EINVAL
     assert L.mx_quant_gain(A16, MIS, 4, 64, 0, A16, A16, None) == EALIGN
-    assert L.mxnorm_linear_fwd(A16, 4, 96, 2, 0.0, A16, A16, 8, A16, A16, None, A16,
+    assert L.mxnorm_linear_fwd(A16, 4, 96, 2, 0.0, A16, A16, 8, A16, A16, None, A16, 0,
                                None) == EUNSUP
+    assert L.mxnorm_linear_fwd(A16, 4, 128, 2, 0.0, A16, A16, 8, A16, A16, None, A16, 3,
+                               None) == EINVAL

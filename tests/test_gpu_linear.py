@@ -84,6 +84,33 @@ def test_matmul_headline_shape_sampled():
     _check(ac, as_, bc, bs, "16384x4096x4096 sampled", sample=1500, seed=3)
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (300, 260, 640), (513, 1000, 1152),
+                                   (256, 255, 256), (1, 3, 128), (2048, 1024, 512)])
+def test_matmul_bf16_output(M, N, K):
+    # the bf16 output is the fp32 result rounded to nearest even (torch's
+    # float -> bfloat16 cast is RNE): bit-equal to rounding the fp32 output,
+    # and within the fp32 bar plus half a bf16 step of the exact product
+    rng = np.random.default_rng(M + 5 * N + K)
+    ac, as_ = rand_mx(rng, M, K)
+    bc, bs = rand_mx(rng, N, K)
+    print("case: bf16 out M=%d N=%d K=%d" % (M, N, K), flush=True)
+    args = (dev(ac), dev(as_), dev(bc), dev(bs))
+    c32 = mxq.mx_matmul(*args)
+    c16 = mxq.mx_matmul(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert c16.dtype == torch.bfloat16
+    r = c32.to(torch.bfloat16)
+    assert torch.equal(c16.view(torch.int16), r.view(torch.int16)), "not RNE of the fp32 result"
+    want = O.mx_matmul(ac, as_, bc, bs)
+    got = c16.float().cpu().numpy().astype(np.float64)
+    mn = np.array([(m, n) for m in range(M) for n in range(N)])
+    A, B = P.mx_dequant(ac, as_), P.mx_dequant(bc, bs)
+    b32 = P.matmul_bound(A, B, mn)
+    bound = b32 + 2.0 ** -8 * (np.abs(want.reshape(-1)) + b32)
+    err = np.abs(got.reshape(-1) - want.reshape(-1))
+    assert (err <= bound).all(), float((err - bound).max())
+
+
 def test_matmul_many_tiles_sampled():
     # 17 x 17 = 289 tiles: more tiles than persistent workgroups, and a count
     # that is not a multiple of the 8 XCDs (the round-robin tile order)
@@ -123,3 +150,6 @@ def test_mxnorm_linear_forward():
     got = out.cpu().numpy().astype(np.float64)
     P.assert_matmul_close(got[mn[:, 0], mn[:, 1]], want[mn[:, 0], mn[:, 1]], A, B, mn,
                           "mxnorm_linear")
+    out16 = mxq.mxnorm_linear_fwd(P.to_device_bf16(xb), wc, ws, p=2, out_dtype=torch.bfloat16)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(out16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
