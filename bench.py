@@ -243,6 +243,19 @@ def main():
               "kernel_source_hash": kernel_hash()}
 
     if not args.no_extras:
+        # the practical ceiling of this byte pattern: the library's reference
+        # kernel with the forward's access pattern and no arithmetic
+        pat_calls = [lambda s=s: L.mxq_stream_pattern(s["x"].data_ptr(), rows, hidden,
+                                                      s["codes"].data_ptr(),
+                                                      s["scales"].data_ptr(),
+                                                      s["rrms"].data_ptr(), sp) for s in sets]
+        npat = max(30, args.steps // 4)
+        _, gpat = time_region(pat_calls, npat, None)
+        pat_bytes = algorithmic_bytes(rows, hidden, w.elem, gamma=False)
+        extras["pattern_stream_us_per_call"] = round(gpat / npat * 1e6, 3)
+        extras["pattern_stream_GBps"] = round(pat_bytes / (gpat / npat) / 1e9, 1)
+        extras["headline_time_over_pattern_stream"] = round(kern_s / (gpat / npat), 4)
+        del pat_calls
         # the same workload without a gain (MXNormLinear mode)
         ng_calls = [lambda s=s: L.mxnorm_fwd(s["x"].data_ptr(), None, rows, hidden, 2, 0.0, w.elem,
                                              s["codes"].data_ptr(), s["scales"].data_ptr(),

@@ -282,6 +282,40 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
 }
 
 // ----------------------------------------------------------------------------------
+// Measurement reference: the byte pattern of k_mxnorm_wave (E4M3, one wave per
+// row, the same lane layout, non-temporal loads and code stores, one scale
+// dword per lane, rho from lane 0) with no arithmetic but an XOR fold, whose
+// result every store carries so that, as in the real kernel, no store can
+// leave before the whole row has arrived.
+// ----------------------------------------------------------------------------------
+template <int STEPS>
+__global__ __launch_bounds__(kThreads) void k_stream_pattern(const uint8_t* __restrict__ x,
+                                                             int64_t rows, int hidden,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             float* __restrict__ rrms) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const uint8_t* xrow = x + row * (int64_t)hidden * 2;
+  uint4 v[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + (uint32_t)(s * kWave + lane) * 16u);
+  uint32_t f = 0;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) f ^= v[s].x;
+  uint8_t* crow = codes + row * (int64_t)hidden;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const u32x2_t o = {v[s].x ^ v[s].y ^ f, v[s].z ^ v[s].w};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(crow + (uint32_t)(s * kWave + lane) * 8u));
+  }
+  if (lane < (hidden >> 7)) reinterpret_cast<uint32_t*>(scales + row * (hidden >> 5))[lane] = f;
+  if (lane == 0) rrms[row] = __uint_as_float(f);
+}
+
+// ----------------------------------------------------------------------------------
 // MXNorm forward for wide rows (4096 < hidden <= 32768): a row is owned by W
 // waves (4/W rows per workgroup); the two row reductions cross waves through
 // LDS.  Lane `lane` of wave `wir` owns chunk (s*W + wir)*64 + lane at step s.
@@ -612,6 +646,21 @@ hipError_t launch_mxnorm(const MxnormArgs& a) {
   if (a.elem == 0)
     return a.gamma ? launch_mxnorm_had<0, true>(a) : launch_mxnorm_had<0, false>(a);
   return a.gamma ? launch_mxnorm_had<1, true>(a) : launch_mxnorm_had<1, false>(a);
+}
+
+hipError_t launch_stream_pattern(const void* x, int64_t rows, int hidden, uint8_t* codes,
+                                 uint8_t* scales, float* rrms, void* stream) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  hipStream_t st = (hipStream_t)stream;
+  switch (hidden) {
+    case 512: hipLaunchKernelGGL(k_stream_pattern<1>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
+    case 1024: hipLaunchKernelGGL(k_stream_pattern<2>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
+    case 2048: hipLaunchKernelGGL(k_stream_pattern<4>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
+    case 4096: hipLaunchKernelGGL(k_stream_pattern<8>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,

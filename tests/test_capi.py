@@ -229,3 +229,17 @@ def test_matmul_argument_checks():
                                None) == EUNSUP
     assert L.mxnorm_linear_fwd(A16, 4, 128, 2, 0.0, A16, A16, 8, A16, A16, None, A16, 3,
                                None) == EINVAL
+
+
+def test_stream_pattern_argument_checks():
+    L = mxq.lib()
+    f = lambda **kw: L.mxq_stream_pattern(kw.get("x", A16), kw.get("rows", 4),
+                                          kw.get("hidden", 4096), kw.get("codes", A16),
+                                          kw.get("scales", A16), kw.get("rrms", A16), None)
+    assert f(hidden=768) == EUNSUP
+    assert f(hidden=0) == EINVAL
+    assert f(rows=-1) == EINVAL
+    assert f(rows=0, x=None) == OK
+    assert f(x=None) == EINVAL
+    assert f(x=MIS) == EALIGN
+    assert f(scales=A16 + 2) == EALIGN

@@ -231,3 +231,28 @@ def test_baseline_shapes(hidden, elem):
     xb, gb = W.generate(33, hidden, "rowscale", seed=hidden + 11)
     _check_baseline(xb, gb, 1e-5, elem, "two-pass D=%d" % hidden)
     _check_baseline(xb, None, 0.0, elem, "two-pass D=%d no gamma" % hidden)
+
+
+def test_stream_pattern_reference_moves_the_bytes():
+    # the measurement reference reads every input word and writes every output
+    # byte of the forward's pattern: check its XOR fold on the host
+    rows, hidden = 37, 4096
+    rng = np.random.default_rng(99)
+    xw = rng.integers(0, 2 ** 32, size=(rows, hidden // 2), dtype=np.uint32)
+    x = torch.from_numpy(xw.view(np.int32)).cuda()
+    codes = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, hidden // 32), dtype=torch.uint8, device="cuda")
+    rr = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    st = mxq.lib().mxq_stream_pattern(x.data_ptr(), rows, hidden, codes.data_ptr(),
+                                      scales.data_ptr(), rr.data_ptr(), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    v = xw.reshape(rows, 8, 64, 4)                       # step, lane, word
+    f = np.bitwise_xor.reduce(v[:, :, :, 0], axis=1)     # [rows, lane]
+    lo = v[:, :, :, 0] ^ v[:, :, :, 1] ^ f[:, None, :]
+    hi = v[:, :, :, 2] ^ v[:, :, :, 3]
+    want = np.stack([lo, hi], axis=-1).reshape(rows, -1).view(np.uint8)
+    assert np.array_equal(codes.cpu().numpy(), want)
+    sw = scales.cpu().numpy().view(np.uint32)
+    assert np.array_equal(sw, f[:, :32])
+    assert np.array_equal(rr.cpu().numpy().view(np.uint32), f[:, 0])
