@@ -311,6 +311,36 @@ def main():
             extras[key + "_algorithmic_GBps"] = round(bb / (gt / nb) / 1e9, 1)
         del bsets
         torch.cuda.empty_cache()
+        # the backward on wider rows (same element count): 8192 x 8192 and
+        # 2048 x 32768, with the gain (2 and 8 waves per row)
+        for (wr, wh) in ((8192, 8192), (2048, 32768)):
+            xw = W.random_rows(wr, wh, 77).astype(np.float32)
+            xwb = W.to_bf16_bits(xw)
+            gwb = W.to_bf16_bits(np.float32(1.0) + np.float32(0.02) *
+                                 W.random_rows(1, wh, 78)[0].astype(np.float32))
+            dwb = W.grad_output(wr, wh, 77)
+            gwd = torch.from_numpy(gwb.view(np.int16)).to(dev)
+            wsets = []
+            for i in range(3):
+                xd = torch.from_numpy(xwb.view(np.int16)).to(dev)
+                rr = torch.empty((wr,), dtype=torch.float32, device=dev)
+                mxq.mxnorm_fwd(xd.view(torch.bfloat16), gwd.view(torch.bfloat16), p=2, rrms=rr)
+                wsets.append(dict(x=xd, dy=torch.from_numpy(dwb.view(np.int16)).to(dev), r=rr,
+                                  dx=torch.empty_like(xd),
+                                  dg=torch.empty((wh,), dtype=torch.float32, device=dev),
+                                  ws=torch.empty((mxq.mxnorm_bwd_workspace_bytes(wr, wh) // 4,),
+                                                 dtype=torch.float32, device=dev)))
+            bc = [lambda s=s: L.mxnorm_bwd(s["x"].data_ptr(), s["dy"].data_ptr(), gwd.data_ptr(),
+                                            s["r"].data_ptr(), wr, wh, s["dx"].data_ptr(),
+                                            s["dg"].data_ptr(), s["ws"].data_ptr(), sp)
+                  for s in wsets]
+            nb = max(30, args.steps // 4)
+            _, gt = time_region(bc, nb, None)
+            key = "mxnorm_bwd_%dx%d" % (wr, wh)
+            extras[key + "_us_per_call"] = round(gt / nb * 1e6, 3)
+            extras[key + "_algorithmic_GBps"] = round(bwd_bytes(wr, wh, True) / (gt / nb) / 1e9, 1)
+            del wsets
+            torch.cuda.empty_cache()
 
         # MXNormLinear on the headline matrix: the gain folded into a square
         # weight (hidden x hidden, cast once), then per step mxnorm_fwd with no

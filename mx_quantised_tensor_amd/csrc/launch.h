@@ -43,10 +43,12 @@ hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, 
                                 int elem, uint8_t* codes, uint8_t* scales, void* stream);
 
 // Straight-through MXNorm backward.  hidden <= kBwdMaxHidden.
-constexpr int kBwdMaxHidden = 4096;
-// Persistent workgroups of the backward with a gain (4 waves each); tuned on
+constexpr int kBwdMaxHidden = 32768;
+// Persistent workgroups of the backward with a gain (192 of 4 waves at hidden
+// <= 4096; 512 of 2 waves, 256 of 4 or 8 waves for wider rows); tuned on
 // MI355X, where fewer rows in flight stream faster for this kernel.
 constexpr int64_t kBwdMaxGroups = 192;
+constexpr int64_t kBwdMaxPartials = 512;  // most partial dgamma rows (W = 2)
 
 struct BwdLaunch {
   const void* x;
@@ -61,6 +63,7 @@ struct BwdLaunch {
   void* stream;
 };
 
+int bwd_waves_per_row(int hidden);
 int64_t bwd_groups(int64_t rows, int hidden);
 hipError_t launch_mxnorm_bwd(const BwdLaunch& l);
 

@@ -25,7 +25,14 @@
 //     by column in a fixed order.  Both orders depend only on (rows, hidden),
 //     so results are run-to-run reproducible;
 //   * without a gain every wave takes one row (four per workgroup), as in the
-//     forward.
+//     forward;
+//   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
+//     workgroup of W waves), lane `lane` of wave `wir` holding chunk
+//     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
+//     of x.g are added through LDS in wave order.  With a gain the workgroups
+//     are persistent over rows (512 of 2 waves, 256 of 4 or 8 waves: measured
+//     best); each wave owns distinct columns, so it writes its part of the
+//     workgroup's partial row directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,7 +47,7 @@ constexpr int kBwdThreads = 256;  // 4 waves per workgroup without a gain
 constexpr int kColsumThreads = 256;
 constexpr int kColsumCols = 16;    // columns per workgroup of the partial-row sum
 constexpr int kColsumSlices = 64;  // partial rows b = slice + 64 k per thread
-constexpr int kColsumLoads = (int)((kBwdMaxGroups + kColsumSlices - 1) / kColsumSlices);
+constexpr int kColsumLoads = (int)((kBwdMaxPartials + kColsumSlices - 1) / kColsumSlices);
 
 constexpr int kBwdWaves = 4;  // waves per workgroup of the persistent (gain) kernel
 
@@ -86,12 +93,15 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, int64_t row, const ui
   for (int s = 0; s < STEPS; ++s) dv[s] = load_nt16(a.dy + base + choff[s]);
 }
 
-// dx of one row (and its dgamma contribution added to acc).
-template <bool GAMMA, int STEPS>
+// dx of one row (and its dgamma contribution added to acc).  W > 1: the row is
+// shared by the W waves of the workgroup; s_dot (2 W floats, alternating
+// halves by row parity `par`) carries their partial sums of x.g.
+template <bool GAMMA, int STEPS, int W = 1>
 __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
                                         const uint32_t (&choff)[STEPS], const bool (&act)[STEPS],
                                         const uint4* s_gamma, uint4 (&xv)[STEPS],
-                                        uint4 (&dv)[STEPS], float (&acc)[GAMMA ? STEPS : 1][8]) {
+                                        uint4 (&dv)[STEPS], float (&acc)[GAMMA ? STEPS : 1][8],
+                                        float* s_dot = nullptr, int wir = 0, int par = 0) {
   // rho through the constant address space: a scalar load, so waiting for it
   // never waits for vector loads issued after this row's
   const float rho = ((const __attribute__((address_space(4))) float*)a.rrms)[row];
@@ -106,7 +116,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
     widen8(dv[s], g);
     if constexpr (GAMMA) {
       float gf[8];
-      widen8(s_gamma[s * kWave + lane], gf);
+      widen8(s_gamma[choff[s] >> 4], gf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) g[i] = g[i] * gf[i];  // exact: 8-bit x 8-bit significands
     }
@@ -114,6 +124,16 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
     for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(xf[i], g[i], dot);
   }
   dot = wave_sum_f32(dot);
+  if constexpr (W > 1) {
+    // The other half of s_dot is the next row's, and a wave rewrites this
+    // half two rows later, after every wave has passed the next row's barrier
+    // (and so has read this half).
+    if (lane == 0) s_dot[par * W + wir] = dot;
+    __syncthreads();
+    dot = s_dot[par * W];
+#pragma unroll
+    for (int w = 1; w < W; ++w) dot += s_dot[par * W + w];
+  }
   // Keep only the packed row across the reduction: the barrier stops the
   // compiler from holding the widened products of the first pass (64 more
   // VGPRs); the second pass widens again.
@@ -132,7 +152,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
     widen8(dv[s], dyf);
     float gf[8];
     if constexpr (GAMMA) {
-      widen8(s_gamma[s * kWave + lane], gf);
+      widen8(s_gamma[choff[s] >> 4], gf);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -231,7 +251,86 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
   }
 }
 
-// dgamma_j = sum over the G <= kBwdMaxGroups partial rows, in a fixed order.
+// Rows of 4096 < hidden <= 4096 W: a workgroup of W waves owns one row at a
+// time (8 chunks per lane).
+template <bool GAMMA, int W, bool FULL>
+__global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
+  constexpr int STEPS = 8;
+  const int lane = threadIdx.x & 63;
+  const int wir = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunk = a.hidden >> 3;
+  uint32_t choff[STEPS];
+  bool act[STEPS];
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int ch = (s * W + wir) * kWave + lane;
+    act[s] = FULL || ch < nchunk;
+    choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;
+  }
+  __shared__ float s_dot[2 * W];
+  __shared__ uint4 s_gamma[GAMMA ? STEPS * W * kWave : 1];
+  if constexpr (GAMMA) {
+    for (int c = threadIdx.x; c < STEPS * W * kWave; c += W * kWave)
+      s_gamma[c] = *reinterpret_cast<const uint4*>(a.gamma + (uint32_t)min(c, nchunk - 1) * 16u);
+    __syncthreads();
+  }
+  float acc[GAMMA ? STEPS : 1][8];
+#pragma unroll
+  for (int s = 0; s < (GAMMA ? STEPS : 1); ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[s][i] = 0.0f;
+
+  const int64_t stride = gridDim.x;
+  int64_t row = blockIdx.x;
+  if constexpr (GAMMA && W == 8) {
+    // 8 waves per workgroup leave 256 registers per wave: one register set
+    // (the other waves of the SIMD keep loads in flight)
+    int par = 0;
+    for (; row < a.rows; row += stride) {
+      uint4 xv[STEPS], dv[STEPS];
+      load_row<STEPS>(a, row, choff, xv, dv);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xv, dv, acc, s_dot, wir, par);
+      par ^= 1;
+    }
+  } else if constexpr (GAMMA) {
+    // as in k_mxnorm_bwd: two register sets, the next row's loads in flight
+    uint4 xa[STEPS], da[STEPS], xb[STEPS], db[STEPS];
+    int par = 0;
+    if (row < a.rows) load_row<STEPS>(a, row, choff, xa, da);
+    while (row < a.rows) {
+      const int64_t r1 = row + stride;
+      load_row<STEPS>(a, r1 < a.rows ? r1 : row, choff, xb, db);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xa, da, acc, s_dot, wir, par);
+      par ^= 1;
+      row = r1;
+      if (row >= a.rows) break;
+      const int64_t r2 = row + stride;
+      load_row<STEPS>(a, r2 < a.rows ? r2 : row, choff, xa, da);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xb, db, acc, s_dot, wir, par);
+      par ^= 1;
+      row = r2;
+    }
+  }
+  if constexpr (GAMMA) {
+    // this wave's columns of the workgroup's partial row
+    float* prow = a.partial + (int64_t)blockIdx.x * a.hidden;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      if (!act[s]) continue;
+      float4* dst = reinterpret_cast<float4*>(prow + (choff[s] >> 4) * 8);
+      dst[0] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+      dst[1] = make_float4(acc[s][4], acc[s][5], acc[s][6], acc[s][7]);
+    }
+  } else {
+    if (row < a.rows) {
+      uint4 xv[STEPS], dv[STEPS];
+      load_row<STEPS>(a, row, choff, xv, dv);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xv, dv, acc, s_dot, wir, 0);
+    }
+  }
+}
+
+// dgamma_j = sum over the G <= kBwdMaxPartials partial rows, in a fixed order.
 // Thread (slice, q) of a workgroup loads the float4 of columns 4q..4q+3 of
 // partial rows slice, slice + 64, ... (all loads issued before the adds) and
 // adds them in that order; the 64 slice sums of a column are then added in
@@ -287,8 +386,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, int groups, void* stream) {
   return hipGetLastError();
 }
 
+template <bool GAMMA, int W>
+hipError_t launch_bwd_wide_t(const BwdArgs& a, int groups, void* stream) {
+  if (a.hidden == 4096 * W)
+    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, true>), dim3(groups), dim3(W * 64), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, false>), dim3(groups), dim3(W * 64), 0,
+                       (hipStream_t)stream, a);
+  return hipGetLastError();
+}
+
 template <bool GAMMA>
 hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
+  if (a.hidden > 16384) return launch_bwd_wide_t<GAMMA, 8>(a, groups, stream);
+  if (a.hidden > 8192) return launch_bwd_wide_t<GAMMA, 4>(a, groups, stream);
+  if (a.hidden > 4096) return launch_bwd_wide_t<GAMMA, 2>(a, groups, stream);
   const int nchunk = a.hidden / 8;
   if (nchunk <= 64) return launch_bwd_t<GAMMA, 1>(a, groups, stream);
   if (nchunk <= 128) return launch_bwd_t<GAMMA, 2>(a, groups, stream);
@@ -298,10 +411,20 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
 
 }  // namespace
 
+int bwd_waves_per_row(int hidden) {
+  return hidden > 16384 ? 8 : hidden > 8192 ? 4 : hidden > 4096 ? 2 : 1;
+}
+
 int64_t bwd_groups(int64_t rows, int hidden) {
-  (void)hidden;
-  const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
-  return need < kBwdMaxGroups ? need : kBwdMaxGroups;
+  const int w = bwd_waves_per_row(hidden);
+  if (w == 1) {
+    const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
+    return need < kBwdMaxGroups ? need : kBwdMaxGroups;
+  }
+  // measured on MI355X at 16384 x 4096 / W rows (the partial-row sum included):
+  // 512 workgroups for W = 2, 256 for W = 4 and W = 8
+  const int64_t cap = w == 8 ? 256 : 1024 / w;
+  return rows < cap ? rows : cap;
 }
 
 hipError_t launch_mxnorm_bwd(const BwdLaunch& l) {
@@ -317,7 +440,8 @@ hipError_t launch_mxnorm_bwd(const BwdLaunch& l) {
   a.partial = l.workspace;
   // with a gain the workgroups are persistent (one dgamma partial row each);
   // without one every wave takes a single row, as in the forward
-  const int groups = (int)(l.gamma ? bwd_groups(l.rows, l.hidden) : (l.rows + 3) / 4);
+  const int groups = (int)(l.gamma ? bwd_groups(l.rows, l.hidden)
+                          : bwd_waves_per_row(l.hidden) == 1 ? (l.rows + 3) / 4 : l.rows);
   if (groups > 0) {
     const hipError_t e = l.gamma ? launch_bwd_steps<true>(a, groups, l.stream)
                                  : launch_bwd_steps<false>(a, groups, l.stream);

@@ -109,7 +109,7 @@ def _bwd(x=A16, dy=A16, g=None, rrms=A16, rows=4, hidden=64, dx=A16, dg=None, ws
 def test_hidden_above_limit_unsupported():
     assert _mxq(hidden=mxq.MAX_HIDDEN + 32) == EUNSUP
     assert _mxn(hidden=mxq.MAX_HIDDEN * 2) == EUNSUP
-    assert _bwd(hidden=4096 + 32) == EUNSUP
+    assert _bwd(hidden=32768 + 32) == EUNSUP
 
 
 def test_row_count_limit():
@@ -141,7 +141,13 @@ def test_bwd_workspace_size():
     assert ws(1, 64) == 64 * 4            # one workgroup
     assert ws(5, 64) == 2 * 64 * 4        # ceil(5 / 4) workgroups of 4 waves
     assert ws(16384, 4096) == 192 * 4096 * 4
-    assert ws(16, 8192) == 0 and ws(16, 48) == 0 and ws(-1, 64) == 0
+    # wider rows: one row at a time per workgroup of W waves, 512 workgroups
+    # at most for W = 2 and 256 for W = 4, 8
+    assert ws(16, 8192) == 16 * 8192 * 4
+    assert ws(16384, 8192) == 512 * 8192 * 4      # W = 2
+    assert ws(16384, 12288) == 256 * 12288 * 4    # W = 4
+    assert ws(16384, 32768) == 256 * 32768 * 4    # W = 8
+    assert ws(16, 32800) == 0 and ws(16, 48) == 0 and ws(-1, 64) == 0
 
 
 def test_negative_rows_and_bad_elem():

@@ -57,6 +57,26 @@ def test_bwd_shapes(hidden, with_gamma):
         _check(xb, dyb, gb, rho, "rows=%d hidden=%d gamma=%s" % (rows, hidden, with_gamma))
 
 
+@pytest.mark.parametrize("with_gamma", [True, False])
+@pytest.mark.parametrize("hidden", [4128, 6144, 8192, 8224, 12288, 16384, 20480, 32768])
+def test_bwd_wide_rows(hidden, with_gamma):
+    # 2, 4 or 8 waves per row, full and ragged last steps
+    for rows in (1, 5, 67):
+        xb, dyb, gb, rho = _inputs(rows, hidden, with_gamma=with_gamma, seed=hidden + rows)
+        _check(xb, dyb, gb, rho, "rows=%d hidden=%d gamma=%s" % (rows, hidden, with_gamma))
+
+
+@pytest.mark.parametrize("hidden", [8192, 16384, 32768])
+def test_bwd_wide_rows_persistent(hidden):
+    # more rows than workgroups (512 or 256 of them): each workgroup takes several
+    # rows, alternating register sets (W = 2, 4) or one set (W = 8)
+    rows = {8192: 1200, 16384: 600, 32768: 600}[hidden]
+    xb, dyb, gb, rho = _inputs(rows, hidden, kind="rowscale", seed=hidden)
+    dx1, dg1 = _check(xb, dyb, gb, rho, "persistent rows=%d hidden=%d" % (rows, hidden))
+    dx2, dg2 = _run(xb, dyb, gb, rho)
+    assert np.array_equal(dx1, dx2) and np.array_equal(dg1.view(np.uint32), dg2.view(np.uint32))
+
+
 @pytest.mark.parametrize("kind", ["outlier", "rowscale", "t3"])
 def test_bwd_many_rows_persistent(kind):
     # more rows than the persistent grid holds waves: every wave takes several rows
