@@ -56,7 +56,7 @@ typedef enum {
     MXQ_OK = 0,
     MXQ_EINVAL = -1,        /* bad shape, NULL pointer, bad p / c / eps / had */
     MXQ_EALIGN = -2,        /* a pointer is not aligned as required above */
-    MXQ_EUNSUPPORTED = -3,  /* valid arguments outside what this build supports */
+    MXQ_EUNSUPPORTED = -3,  /* valid arguments outside what the library supports */
     MXQ_EHIP = -4           /* the HIP runtime refused the launch */
 } mxq_status;
 

@@ -246,7 +246,7 @@ const char* mxq_status_str(mxq_status s) {
     case MXQ_OK: return "MXQ_OK";
     case MXQ_EINVAL: return "MXQ_EINVAL: invalid argument";
     case MXQ_EALIGN: return "MXQ_EALIGN: pointer misaligned";
-    case MXQ_EUNSUPPORTED: return "MXQ_EUNSUPPORTED: shape outside this build's limits";
+    case MXQ_EUNSUPPORTED: return "MXQ_EUNSUPPORTED: shape outside the library's limits";
     case MXQ_EHIP: return "MXQ_EHIP: HIP launch failed";
   }
   return "MXQ_UNKNOWN";
