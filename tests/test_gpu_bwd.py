@@ -137,3 +137,25 @@ def test_bwd_on_side_stream():
     ref_dx, ref_dg = O.mxnorm_bwd(xb, dyb, gb, rho)
     P.assert_bwd_close(P.from_device(dx.view(torch.int16)).view(np.uint16), P.from_device(dg),
                        xb, dyb, gb, rho, ref_dx, ref_dg, "side stream")
+
+
+def test_bwd_maximum_rows_sampled():
+    # 2^24 - 1 rows (the C ABI's limit), hidden 64, no gain: dx on sampled rows
+    rows, hidden = (1 << 24) - 1, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(32)
+    x = torch.randn(rows, hidden, device="cuda", generator=gen).to(torch.bfloat16)
+    dy = torch.randn(rows, hidden, device="cuda", generator=gen).to(torch.bfloat16)
+    r = (torch.rand(rows, device="cuda", generator=gen) + 0.5).float()
+    print("case: mxnorm_bwd rows=%d hidden=%d" % (rows, hidden), flush=True)
+    dx, _ = mxq.mxnorm_bwd(x, dy, r, None)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(32)
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 3000), [0, rows - 1]]))
+    ti = torch.from_numpy(idx).cuda()
+    xb = x[ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    dyb = dy[ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    rho = r[ti].cpu().numpy()
+    ref_dx, _ = O.mxnorm_bwd(xb, dyb, None, rho)
+    got = dx[ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    P.assert_bwd_close(got, None, xb, dyb, None, rho, ref_dx, None, "bwd max rows")

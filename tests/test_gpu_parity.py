@@ -256,3 +256,24 @@ def test_stream_pattern_reference_moves_the_bytes():
     sw = scales.cpu().numpy().view(np.uint32)
     assert np.array_equal(sw, f[:, :32])
     assert np.array_equal(rr.cpu().numpy().view(np.uint32), f[:, 0])
+
+
+def test_mxnorm_maximum_rows_sampled():
+    # the largest row count the C ABI accepts (2^24 - 1: the grid then holds
+    # 2^22 workgroups), hidden 64, checked on sampled rows that the oracle
+    # computes one by one (the first and last rows included)
+    rows, hidden = (1 << 24) - 1, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    x = (torch.randn(rows, hidden, device="cuda", generator=gen) * 3.0).to(torch.bfloat16)
+    print("case: mxnorm_fwd rows=%d hidden=%d" % (rows, hidden), flush=True)
+    codes, scales, rho = mxq.mxnorm_fwd(x, None, p=2, c=C_DEF[2], elem=O.E4M3)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 3000), [0, 1, rows - 2, rows - 1]]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = x[ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    oc, os_, orr = O.mxnorm_fwd(xs, None, 2, C_DEF[2], O.E4M3)
+    P.assert_rho_equal(rho[ti].cpu().numpy(), orr, "max rows")
+    P.assert_scales_equal(scales[ti].cpu().numpy(), os_, "max rows")
+    P.assert_codes(codes[ti].cpu().numpy(), oc, os_, O.E4M3, exact=True, what="max rows")
