@@ -385,6 +385,28 @@ def main():
         _, gt = time_region(mmh, nm, None)
         extras["mx_matmul_bf16_out_us_per_call"] = round(gt / nm * 1e6, 3)
         extras["mx_matmul_bf16_out_TFLOPs"] = round(flops / (gt / nm) / 1e12, 1)
+        # The unfused layer MXNormLinear replaces: RMSNorm with its gain to a
+        # bf16 y, the MX cast of y (the two-pass baseline), then the matmul
+        # with the plain MX cast of W.
+        wpc = torch.empty((hidden, hidden), dtype=torch.uint8, device=dev)
+        wps = torch.empty((hidden, hidden // 32), dtype=torch.uint8, device=dev)
+        mxq.mx_quant(wdev.view(torch.bfloat16), codes=wpc, scales=wps)
+        ys = [torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev) for _ in lsets]
+
+        def unfused(s, y):
+            rc = L.rmsnorm_mxquant_fwd(s["x"].data_ptr(), gb_dev.data_ptr(), rows, hidden, 1e-5,
+                                       mxq.E4M3, y.data_ptr(), s["xc"].data_ptr(),
+                                       s["xs"].data_ptr(), None, sp)
+            return rc or L.mx_matmul(s["xc"].data_ptr(), s["xs"].data_ptr(), wpc.data_ptr(),
+                                     wps.data_ptr(), rows, hidden, hidden, s["out"].data_ptr(),
+                                     mxq.OUT_F32, sp)
+        unf = [lambda s=s, y=y: unfused(s, y) for s, y in zip(lsets, ys)]
+        _, gt = time_region(unf, nm, None)
+        extras["rmsnorm_mxquant_then_matmul_us_per_call"] = round(gt / nm * 1e6, 3)
+        extras["mxnorm_linear_speedup_vs_unfused"] = round(
+            extras["rmsnorm_mxquant_then_matmul_us_per_call"]
+            / extras["mxnorm_linear_fwd_us_per_call"], 3)
+        del ys, wpc, wps
         del lsets, wdev, wc, wsc
         torch.cuda.empty_cache()
 
