@@ -175,25 +175,131 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
   const int G = (int)gridDim.x;
   const bool by_xcd = ntiles % kXcds == 0 && G % kXcds == 0;
   const int per_x = ntiles / kXcds, xcd = (int)blockIdx.x % kXcds, jx = (int)blockIdx.x / kXcds;
-  for (int it = 0;; ++it) {
-    int t;
+  // Tile of this workgroup's iteration it, or -1 past its last one.
+  auto tile_at = [&](int it) -> int {
     if (by_xcd) {
       const int w = jx + it * (G / kXcds);
-      if (w >= per_x) break;
-      t = xcd * per_x + w;
-    } else {
-      t = (int)blockIdx.x + it * G;
-      if (t >= ntiles) break;
+      return w < per_x ? xcd * per_x + w : -1;
     }
+    const int t = (int)blockIdx.x + it * G;
+    return t < ntiles ? t : -1;
+  };
+  int64_t m0 = 0, n0 = 0;  // origin of the tile whose copies are in flight
+  rsrc_t ra, rb, rsa, rsb;
+  auto set_tile = [&](int t) {
     int tm, tn;
     tile_coords(t, g.tiles_m, g.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    m0 = (int64_t)tm * kTile;
+    n0 = (int64_t)tn * kTile;
     const uint32_t rows_a = (uint32_t)min((int64_t)kTile, g.M - m0);
     const uint32_t rows_b = (uint32_t)min((int64_t)kTile, g.N - n0);
-    const rsrc_t ra = make_rsrc(g.a + m0 * K, rows_a * (uint32_t)K);
-    const rsrc_t rb = make_rsrc(g.b + n0 * K, rows_b * (uint32_t)K);
-    const rsrc_t rsa = make_rsrc(g.as + m0 * KB, rows_a * (uint32_t)KB);
-    const rsrc_t rsb = make_rsrc(g.bs + n0 * KB, rows_b * (uint32_t)KB);
+    ra = make_rsrc(g.a + m0 * K, rows_a * (uint32_t)K);
+    rb = make_rsrc(g.b + n0 * K, rows_b * (uint32_t)K);
+    rsa = make_rsrc(g.as + m0 * KB, rows_a * (uint32_t)KB);
+    rsb = make_rsrc(g.bs + n0 * KB, rows_b * (uint32_t)KB);
+  };
+
+// Copy instruction D (0..15) of copy stage J: operand A for D < 8, B
+// otherwise; 8 rows (64 wave + 8 (D % 8) + lane / 8) x 128 bytes, lane l
+// filling physical chunk l % 8 with the logical chunk that belongs there.
+#define MXQ_GEMM_DATA_OP(J, D)                                                              \
+  do {                                                                                      \
+    const int t_ = (D) & 7;                                                                 \
+    const int rl_ = wave * 64 + t_ * 8 + crow;                                              \
+    const int c_ = cphys ^ crow ^ (t_ & 3);                                                 \
+    const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)K + (uint32_t)((J) * kCopyK + c_ * 16); \
+    const uint32_t dst_ = base + (uint32_t)(((J) & 1) * kBuf) + ((D) >= 8 ? kSlice : 0) +   \
+                          (uint32_t)((wave * 64 + t_ * 8) * kCopyK);                        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds((D) >= 8 ? rb : ra,                            \
+                                             (MXQ_LDS void*)(size_t)dst_, 16, (int)voff_, 0, \
+                                             0, 0);                                         \
+  } while (0)
+
+// Scale copy KOP (0..7) of group GRP: operand A for KOP < 4, B otherwise; 16
+// rows (64 wave + 16 (KOP % 4) + lane / 4), lane l filling position l % 4 of
+// its row's record.  Dwords past the row's end are clamped to its last one
+// (never read).
+#define MXQ_GEMM_SCALE_OP(GRP, KOP)                                                         \
+  do {                                                                                      \
+    const int k_ = (KOP), t_ = k_ & 3;                                                      \
+    const int rl_ = wave * 64 + t_ * 16 + (lane >> 2);                                      \
+    const int q_ = ((lane & 3) - ((2 * t_ + (lane >> 5)) & 3)) & 3;                         \
+    const int gq_ = min(4 * (GRP) + q_, KB / 4 - 1);                                        \
+    const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)KB + (uint32_t)(4 * gq_);              \
+    const uint32_t dst_ = base + kScaleBase + (uint32_t)(mod3(GRP) * kScaleSet) +           \
+                          (k_ >= 4 ? kTile * kScaleRec : 0) +                               \
+                          (uint32_t)((wave * 64 + t_ * 16) * kScaleRec);                    \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(k_ >= 4 ? rsb : rsa,                           \
+                                             (MXQ_LDS void*)(size_t)dst_, 4, (int)voff_, 0, \
+                                             0, 0);                                         \
+  } while (0)
+
+// Copy instruction X (0..17) of stage J: its 16 data copies, then scale
+// copies 2 (J % 4) and 2 (J % 4) + 1 of group J / 4 + 1 (issued once group
+// J / 4 - 2, the set's previous tenant, is no longer read; landed long before
+// stage 4 (J / 4 + 1) is read).
+#define MXQ_GEMM_OP(J, X)                                                                   \
+  do {                                                                                      \
+    if ((X) < 16) MXQ_GEMM_DATA_OP(J, X);                                                   \
+    else MXQ_GEMM_SCALE_OP(((J) >> 2) + 1, 2 * ((J) & 3) + (X) - 16);                       \
+  } while (0)
+
+// Fragment read R (0..23) of sub-stage U into NA/NB (operand chunks) and
+// NSA/NSB (the scale dword of the sub-stage's copy stage).
+#define MXQ_GEMM_READ(U, R, NA, NB, NSA, NSB)                                               \
+  do {                                                                                      \
+    const int ur_ = (U);                                                                    \
+    if ((R) < 16) {                                                                         \
+      const int ii_ = (R) >> 2, h_ = ((R) >> 1) & 1;                                        \
+      const uint32_t b_ = base + (uint32_t)(((ur_ >> 1) & 1) * kBuf) + coff[ur_ & 1][h_];   \
+      if ((R) & 1) NB[ii_][h_] = lds_read16(b_ + b_off[ii_]);                               \
+      else NA[ii_][h_] = lds_read16(b_ + a_off[ii_]);                                       \
+    } else {                                                                                \
+      const int jr_ = ur_ >> 1;                                                             \
+      const uint32_t s_ = base + kScaleBase + (uint32_t)(mod3(jr_ >> 2) * kScaleSet) +      \
+                          (uint32_t)((((jr_ & 3) + srot) & 3) * 4);                         \
+      if ((R) < 20) NSA[(R) - 16] = lds_read4(s_ + as_off[(R) - 16]);                       \
+      else NSB[(R) - 20] = lds_read4(s_ + bs_off[(R) - 20]);                                \
+    }                                                                                       \
+  } while (0)
+
+// Wait for this lane's fragment reads and make their registers visible as
+// written here (the compiler cannot see inside the reads); then move each
+// lane's scale byte of sub-stage U (byte 2 (U % 2) + fh of the dword) to byte 0.
+#define MXQ_GEMM_READ_DONE(U, NA, NB, NSA, NSB)                                             \
+  do {                                                                                      \
+    asm volatile("s_waitcnt lgkmcnt(0)"                                                     \
+                 : "+v"(NA[0][0]), "+v"(NA[0][1]), "+v"(NA[1][0]), "+v"(NA[1][1]),          \
+                   "+v"(NA[2][0]), "+v"(NA[2][1]), "+v"(NA[3][0]), "+v"(NA[3][1]),          \
+                   "+v"(NB[0][0]), "+v"(NB[0][1]), "+v"(NB[1][0]), "+v"(NB[1][1]),          \
+                   "+v"(NB[2][0]), "+v"(NB[2][1]), "+v"(NB[3][0]), "+v"(NB[3][1]),          \
+                   "+v"(NSA[0]), "+v"(NSA[1]), "+v"(NSA[2]), "+v"(NSA[3]), "+v"(NSB[0]),    \
+                   "+v"(NSB[1]), "+v"(NSB[2]), "+v"(NSB[3]));                               \
+    const uint32_t sh_ = 8 * fh + 16 * ((U) & 1);                                           \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
+      NSA[i_] >>= sh_;                                                                      \
+      NSB[i_] >>= sh_;                                                                      \
+    }                                                                                       \
+  } while (0)
+
+// Prologue copies of the tile set by set_tile: stage 0, the first copies of
+// scale groups 0 and 1, stage 1.  Issued once every wave is done reading the
+// LDS of the tile before (or at the start).
+#define MXQ_GEMM_PROLOGUE_ISSUE()                                                           \
+  do {                                                                                      \
+    _Pragma("unroll") for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(0, x);                 \
+    _Pragma("unroll") for (int k = 0; k < 8; ++k) MXQ_GEMM_SCALE_OP(0, k);                  \
+    if (nstages > 1) {                                                                      \
+      _Pragma("unroll") for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(1, x);               \
+    }                                                                                       \
+  } while (0)
+
+  int tile = tile_at(0);
+  if (tile < 0) return;
+  set_tile(tile);
+  MXQ_GEMM_PROLOGUE_ISSUE();
+  for (int it = 0;; ++it) {
+
 
     v16f acc[4][4];
 #pragma unroll
@@ -203,104 +309,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-// Copy instruction D (0..15) of copy stage J: operand A for D < 8, B
-// otherwise; 8 rows (64 wave + 8 (D % 8) + lane / 8) x 128 bytes, lane l
-// filling physical chunk l % 8 with the logical chunk that belongs there.
-#define MXQ_GEMM_DATA_OP(J, D)                                                                \
-    do {                                                                                      \
-      const int t_ = (D) & 7;                                                                 \
-      const int rl_ = wave * 64 + t_ * 8 + crow;                                              \
-      const int c_ = cphys ^ crow ^ (t_ & 3);                                                 \
-      const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)K + (uint32_t)((J) * kCopyK + c_ * 16); \
-      const uint32_t dst_ = base + (uint32_t)(((J) & 1) * kBuf) + ((D) >= 8 ? kSlice : 0) +   \
-                            (uint32_t)((wave * 64 + t_ * 8) * kCopyK);                        \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((D) >= 8 ? rb : ra,                            \
-                                               (MXQ_LDS void*)(size_t)dst_, 16, (int)voff_, 0, \
-                                               0, 0);                                         \
-    } while (0)
-
-// Scale copy KOP (0..7) of group GRP: operand A for KOP < 4, B otherwise; 16
-// rows (64 wave + 16 (KOP % 4) + lane / 4), lane l filling position l % 4 of
-// its row's record.  Dwords past the row's end are clamped to its last one
-// (never read).
-#define MXQ_GEMM_SCALE_OP(GRP, KOP)                                                           \
-    do {                                                                                      \
-      const int k_ = (KOP), t_ = k_ & 3;                                                      \
-      const int rl_ = wave * 64 + t_ * 16 + (lane >> 2);                                      \
-      const int q_ = ((lane & 3) - ((2 * t_ + (lane >> 5)) & 3)) & 3;                         \
-      const int gq_ = min(4 * (GRP) + q_, KB / 4 - 1);                                        \
-      const uint32_t voff_ = (uint32_t)rl_ * (uint32_t)KB + (uint32_t)(4 * gq_);              \
-      const uint32_t dst_ = base + kScaleBase + (uint32_t)(mod3(GRP) * kScaleSet) +           \
-                            (k_ >= 4 ? kTile * kScaleRec : 0) +                               \
-                            (uint32_t)((wave * 64 + t_ * 16) * kScaleRec);                    \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_ >= 4 ? rsb : rsa,                           \
-                                               (MXQ_LDS void*)(size_t)dst_, 4, (int)voff_, 0, \
-                                               0, 0);                                         \
-    } while (0)
-
-// Copy instruction X (0..17) of stage J: its 16 data copies, then scale
-// copies 2 (J % 4) and 2 (J % 4) + 1 of group J / 4 + 1 (issued once group
-// J / 4 - 2, the set's previous tenant, is no longer read; landed long before
-// stage 4 (J / 4 + 1) is read).
-#define MXQ_GEMM_OP(J, X)                                                                     \
-    do {                                                                                      \
-      if ((X) < 16) MXQ_GEMM_DATA_OP(J, X);                                                   \
-      else MXQ_GEMM_SCALE_OP(((J) >> 2) + 1, 2 * ((J) & 3) + (X) - 16);                       \
-    } while (0)
-
-// Fragment read R (0..23) of sub-stage U into NA/NB (operand chunks) and
-// NSA/NSB (the scale dword of the sub-stage's copy stage).
-#define MXQ_GEMM_READ(U, R, NA, NB, NSA, NSB)                                                 \
-    do {                                                                                      \
-      const int ur_ = (U);                                                                    \
-      if ((R) < 16) {                                                                         \
-        const int ii_ = (R) >> 2, h_ = ((R) >> 1) & 1;                                        \
-        const uint32_t b_ = base + (uint32_t)(((ur_ >> 1) & 1) * kBuf) + coff[ur_ & 1][h_];   \
-        if ((R) & 1) NB[ii_][h_] = lds_read16(b_ + b_off[ii_]);                               \
-        else NA[ii_][h_] = lds_read16(b_ + a_off[ii_]);                                       \
-      } else {                                                                                \
-        const int jr_ = ur_ >> 1;                                                             \
-        const uint32_t s_ = base + kScaleBase + (uint32_t)(mod3(jr_ >> 2) * kScaleSet) +      \
-                            (uint32_t)((((jr_ & 3) + srot) & 3) * 4);                         \
-        if ((R) < 20) NSA[(R) - 16] = lds_read4(s_ + as_off[(R) - 16]);                       \
-        else NSB[(R) - 20] = lds_read4(s_ + bs_off[(R) - 20]);                                \
-      }                                                                                       \
-    } while (0)
-
-// Wait for this lane's fragment reads and make their registers visible as
-// written here (the compiler cannot see inside the reads); then move each
-// lane's scale byte of sub-stage U (byte 2 (U % 2) + fh of the dword) to byte 0.
-#define MXQ_GEMM_READ_DONE(U, NA, NB, NSA, NSB)                                               \
-    do {                                                                                      \
-      asm volatile("s_waitcnt lgkmcnt(0)"                                                     \
-                   : "+v"(NA[0][0]), "+v"(NA[0][1]), "+v"(NA[1][0]), "+v"(NA[1][1]),         \
-                     "+v"(NA[2][0]), "+v"(NA[2][1]), "+v"(NA[3][0]), "+v"(NA[3][1]),         \
-                     "+v"(NB[0][0]), "+v"(NB[0][1]), "+v"(NB[1][0]), "+v"(NB[1][1]),         \
-                     "+v"(NB[2][0]), "+v"(NB[2][1]), "+v"(NB[3][0]), "+v"(NB[3][1]),         \
-                     "+v"(NSA[0]), "+v"(NSA[1]), "+v"(NSA[2]), "+v"(NSA[3]), "+v"(NSB[0]),   \
-                     "+v"(NSB[1]), "+v"(NSB[2]), "+v"(NSB[3]));                              \
-      const uint32_t sh_ = 8 * fh + 16 * ((U) & 1);                                           \
-      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
-        NSA[i_] >>= sh_;                                                                      \
-        NSB[i_] >>= sh_;                                                                      \
-      }                                                                                       \
-    } while (0)
-
-    // Prologue: stages 0 and 1 (and scale groups 0 and 1's first copies)
-    // out, wait for stage 0, read sub-stage 0.
-    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's LDS
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(0, x);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) MXQ_GEMM_SCALE_OP(0, k);
-    if (nstages > 1) {
-#pragma unroll
-      for (int x = 0; x < kCopyOps; ++x) MXQ_GEMM_OP(1, x);
-      wait_vmcnt<kCopyOps>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // Stage 0 (and scale group 0) landed: the previous tile's stores, issued
+    // after these copies, may still be in flight behind them.
+    if (nstages > 1) wait_vmcnt<kCopyOps>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 
     v4i xa[4][2], xb[4][2], ya[4][2], yb[4][2];
@@ -316,36 +328,36 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 // Even sub-stages end by waiting for stage j + 1 and a barrier.  The empty
 // statement after each instruction keeps it ahead of the memory instructions
 // that follow (it touches no memory, so the compiler would move it freely).
-#define MXQ_GEMM_SUBSTAGE(U, ODD, CA, CB, CSA, CSB, NA, NB, NSA, NSB)                          \
-    do {                                                                                      \
-      const int u_ = (U);                                                                     \
-      const int j_ = u_ >> 1;                                                                 \
-      const bool rd_ = (ODD) ? (j_ + 1 < nstages) : true;                                     \
-      const bool cp_ = (ODD) && (j_ + 2 < nstages);                                           \
-      _Pragma("unroll") for (int m = 0; m < 16; ++m) {                                        \
-        if (cp_) {                                                                            \
-          MXQ_GEMM_OP(j_ + 2, m);                                                             \
-          if (m < 2) MXQ_GEMM_OP(j_ + 2, 16 + m);                                             \
-        }                                                                                     \
-        if (m < 12 && rd_) {                                                                  \
-          MXQ_GEMM_READ(u_ + 1, 2 * m, NA, NB, NSA, NSB);                                     \
-          MXQ_GEMM_READ(u_ + 1, 2 * m + 1, NA, NB, NSA, NSB);                                 \
-        }                                                                                     \
-        const int i = m >> 2, j = m & 3;                                                      \
-        const v8i va = {CA[i][0].x, CA[i][0].y, CA[i][0].z, CA[i][0].w,                       \
-                        CA[i][1].x, CA[i][1].y, CA[i][1].z, CA[i][1].w};                      \
-        const v8i vb = {CB[j][0].x, CB[j][0].y, CB[j][0].z, CB[j][0].w,                       \
-                        CB[j][1].x, CB[j][1].y, CB[j][1].z, CB[j][1].w};                      \
+#define MXQ_GEMM_SUBSTAGE(U, ODD, CA, CB, CSA, CSB, NA, NB, NSA, NSB)                       \
+    do {                                                                                    \
+      const int u_ = (U);                                                                   \
+      const int j_ = u_ >> 1;                                                               \
+      const bool rd_ = (ODD) ? (j_ + 1 < nstages) : true;                                   \
+      const bool cp_ = (ODD) && (j_ + 2 < nstages);                                         \
+      _Pragma("unroll") for (int m = 0; m < 16; ++m) {                                      \
+        if (cp_) {                                                                          \
+          MXQ_GEMM_OP(j_ + 2, m);                                                           \
+          if (m < 2) MXQ_GEMM_OP(j_ + 2, 16 + m);                                           \
+        }                                                                                   \
+        if (m < 12 && rd_) {                                                                \
+          MXQ_GEMM_READ(u_ + 1, 2 * m, NA, NB, NSA, NSB);                                   \
+          MXQ_GEMM_READ(u_ + 1, 2 * m + 1, NA, NB, NSA, NSB);                               \
+        }                                                                                   \
+        const int i = m >> 2, j = m & 3;                                                    \
+        const v8i va = {CA[i][0].x, CA[i][0].y, CA[i][0].z, CA[i][0].w,                     \
+                        CA[i][1].x, CA[i][1].y, CA[i][1].z, CA[i][1].w};                    \
+        const v8i vb = {CB[j][0].x, CB[j][0].y, CB[j][0].z, CB[j][0].w,                     \
+                        CB[j][1].x, CB[j][1].y, CB[j][1].z, CB[j][1].w};                    \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[i][j], 0, 0, 0, \
                                                                     (int)CSA[i], 0, (int)CSB[j]); \
-        asm volatile("" ::"a"(acc[i][j]));                                                    \
-      }                                                                                       \
-      if (rd_) MXQ_GEMM_READ_DONE(u_ + 1, NA, NB, NSA, NSB);                                  \
-      if (!(ODD) && j_ + 1 < nstages) {                                                       \
-        wait_vmcnt<0>();                                                                      \
-        __builtin_amdgcn_s_barrier();                                                         \
-        asm volatile("" ::: "memory");                                                        \
-      }                                                                                       \
+        asm volatile("" ::"a"(acc[i][j]));                                                  \
+      }                                                                                     \
+      if (rd_) MXQ_GEMM_READ_DONE(u_ + 1, NA, NB, NSA, NSB);                                \
+      if (!(ODD) && j_ + 1 < nstages) {                                                     \
+        wait_vmcnt<0>();                                                                    \
+        __builtin_amdgcn_s_barrier();                                                       \
+        asm volatile("" ::: "memory");                                                      \
+      }                                                                                     \
     } while (0)
 
     for (int u = 0; u < 2 * nstages; u += 2) {
@@ -353,15 +365,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
       MXQ_GEMM_SUBSTAGE(u + 1, 1, ya, yb, ysa, ysb, xa, xb, xsa, xsb);
     }
 #undef MXQ_GEMM_SUBSTAGE
-#undef MXQ_GEMM_READ_DONE
-#undef MXQ_GEMM_READ
-#undef MXQ_GEMM_OP
-#undef MXQ_GEMM_SCALE_OP
-#undef MXQ_GEMM_DATA_OP
+
+    // Every wave is done reading this tile's LDS: the next tile's first copies
+    // go out now and land while this tile's results are stored.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int64_t em0 = m0, en0 = n0;
+    tile = tile_at(it + 1);
+    if (tile >= 0) {
+      set_tile(tile);
+      MXQ_GEMM_PROLOGUE_ISSUE();
+    }
 
     // epilogue: lane l, register r -> row (r%4) + 8(r/4) + 4(l/32), column l%32
-    const int64_t row0 = m0 + wm * 128 + 4 * fh, col0 = n0 + wn * 128 + fr;
-    const bool full = m0 + kTile <= g.M && n0 + kTile <= g.N;
+    const int64_t row0 = em0 + wm * 128 + 4 * fh, col0 = en0 + wn * 128 + fr;
+    const bool full = em0 + kTile <= g.M && en0 + kTile <= g.N;
     if (!BF16 && full) {
       float* cb = static_cast<float*>(g.c) + row0 * g.N + col0;
 #pragma unroll
@@ -375,8 +393,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
     } else if (BF16 && full && (g.N & 1) == 0) {
       // Registers r, r + 1 (r even) hold rows R, R + 1 of this lane's column.
       // The even lane of a pair stores columns (2c, 2c + 1) of row R, the odd
-      // lane those of row R + 1: each sends its partner the value it lacks.
+      // lane those of row R + 1.  Each lane rounds its two rows to one bf16
+      // pair, swaps the pair with its partner, and one byte permute picks the
+      // halves it stores: (own R, partner R) on the even lane, (partner R + 1,
+      // own R + 1) on the odd one.
       const bool odd = (lane & 1) != 0;
+      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // bytes of {partner, own}
       __bf16* cb = static_cast<__bf16*>(g.c) + (row0 + (odd ? 1 : 0)) * g.N + (col0 & ~(int64_t)1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -385,12 +407,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
           __bf16* crow_p = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-            const float send = odd ? v0 : v1;
-            const float recv = __int_as_float(__builtin_amdgcn_update_dpp(
-                0, __float_as_int(send), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, false));
-            const bf16x2 pk = {(__bf16)(odd ? recv : v0), (__bf16)(odd ? v1 : recv)};
-            __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, pk),
+            const bf16x2 own = {(__bf16)acc[i][j][r], (__bf16)acc[i][j][r + 1]};
+            const uint32_t ow = __builtin_bit_cast(uint32_t, own);
+            const uint32_t pw = (uint32_t)__builtin_amdgcn_mov_dpp(
+                (int)ow, 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, true);
+            __builtin_nontemporal_store(__builtin_amdgcn_perm(pw, ow, sel),
                                         reinterpret_cast<uint32_t*>(crow_p + j * 32));
           }
         }
@@ -410,7 +431,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
           }
         }
     }
+    if (tile < 0) break;
   }
+#undef MXQ_GEMM_PROLOGUE_ISSUE
+#undef MXQ_GEMM_READ_DONE
+#undef MXQ_GEMM_READ
+#undef MXQ_GEMM_OP
+#undef MXQ_GEMM_SCALE_OP
+#undef MXQ_GEMM_DATA_OP
 }
 
 }  // namespace
