@@ -12,10 +12,11 @@
 //   * a lane owns 8 consecutive bf16 (one 16-byte load); a quad of lanes owns
 //     a 32-element MX block, so block reductions are two quad DPP steps;
 //   * one wavefront owns a whole row (hidden <= 4096) and keeps it in VGPRs
-//     between the row statistic and the cast -- no barriers, ~60 VGPRs, 8
-//     waves per SIMD to keep HBM requests in flight;
+//     between the row statistic and the cast -- one barrier (after the gain
+//     copy), at most 64 VGPRs, 8 waves per SIMD to keep HBM requests in flight;
 //   * x is loaded and the codes stored non-temporally (each byte is touched
-//     once); the gain is requested with the row and comes from L2;
+//     once); the gain comes from L2, staged once per workgroup in LDS by
+//     LDS-DMA loads (wide rows: requested into VGPRs once the row has arrived);
 //   * workgroups keep the hardware's round-robin spread over the 8 XCDs, so
 //     the whole chip sweeps one contiguous region of HBM at a time (giving
 //     each XCD its own contiguous range of rows measured ~5% slower).
@@ -44,8 +45,16 @@ struct Elem<1> {  // E2M1: largest power of two 2^2 (6 = 1.5 * 2^2)
 };
 
 // ---- streaming memory access ----------------------------------------------------
+#define MXQ_LDS __attribute__((address_space(3)))
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw buffer over `bytes` bytes at p (stride 0): loads at or past `bytes`
+// read as zero.
+__device__ __forceinline__ rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -188,12 +197,12 @@ struct WaveArgs {
   int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
 };
 
-// The whole forward of one row held in VGPRs (v: the row, gr: the gain).
+// The whole forward of one row held in VGPRs (v: the row; s_gain: the gain,
+// staged in LDS, chunk s * 64 + lane at index s * 64 + lane).
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lane,
                                          const bool (&act)[STEPS], const uint4 (&v)[STEPS],
-                                         const uint4 (&gr)[GAMMA ? STEPS : 1],
-                                         uint32_t* __restrict__ s_sc) {
+                                         const uint4* s_gain, uint32_t* __restrict__ s_sc) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   const int K = a.hidden >> 5;
@@ -223,8 +232,9 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     if (!FULL && !act[s]) continue;  // quad-uniform; the DPP inside stays in the quad
+    const uint4 gv = GAMMA ? s_gain[s * kWave + lane] : make_uint4(0, 0, 0, 0);
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(
-        v[s], gr[GAMMA ? s : 0], rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
+        v[s], gv, rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc)[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
   // the scale bytes written above are read back by other lanes of the wave
@@ -254,35 +264,49 @@ __device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[ST
   }
 }
 
+// The gain is staged once per workgroup in LDS by gfx950's LDS-DMA buffer loads
+// (no VGPRs: 53 instead of 78 at hidden 4096, so 8 waves per SIMD instead of
+// 6, and a quarter of the gain's L2 reads), issued ahead of the row loads; one
+// barrier after they land.  Measured at 16384 x 4096 against requesting the
+// whole gain into VGPRs per wave: 34.0 against 34.6 us (H16 -> E2M1 at 32768
+// rows: 60.9 against 62.6 us).
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
+  __shared__ uint4 s_gain[GAMMA ? STEPS * kWave : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= a.rows) return;  // whole wave; no barriers in this kernel
+  const bool row_ok = row < a.rows;  // waves past the end still copy the gain and meet the barrier
 
   uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
   bool act[STEPS];
   lane_chunks<STEPS, FULL>(lane, a.hidden >> 3, act, choff);
-  const uint8_t* xrow = a.x + row * (int64_t)a.hidden * 2;
+  if constexpr (GAMMA) {
+    // wave w copies steps w, w + 4 of the gain; chunks past the row end read
+    // as zero (buffer range) and are never used
+    const rsrc_t rg = row_rsrc(a.gamma, (uint32_t)a.hidden * 2u);
+#pragma unroll
+    for (int j = 0; j < (STEPS + 3) / 4; ++j) {
+      const int s = j * 4 + wave;
+      if (s < STEPS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + s * kWave * 16), 16,
+            (int)((uint32_t)(s * kWave + lane) * 16u), 0, 0, 0);
+    }
+  }
+  const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
   uint4 v[STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + choff[s]);
-  // The gain (L1/L2-resident): for full 4096-wide rows it is requested once
-  // the row has arrived, when the row statistic starts, and arrives while it
-  // is computed (requesting it with the row measured 0.7% slower: its requests
-  // sit between the row requests of the other waves); shorter rows have too
-  // short a statistic to hide it, so it is requested with the row.
-  uint4 gr[GAMMA ? STEPS : 1];
   if constexpr (GAMMA) {
-    if constexpr (STEPS == 8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(a.gamma + choff[s]);
-  } else {
-    gr[0] = make_uint4(0, 0, 0, 0);
+    // the copies were issued before the STEPS row loads: at most STEPS loads
+    // outstanding means the copies have landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(STEPS) : "memory");
+    __syncthreads();
   }
-  wave_row<ELEM, GAMMA, HAD, STEPS, FULL, SRC>(a, row, lane, act, v, gr, s_sc[wave]);
+  if (!row_ok) return;  // whole wave, after the only barrier
+  wave_row<ELEM, GAMMA, HAD, STEPS, FULL, SRC>(a, row, lane, act, v, s_gain, s_sc[wave]);
 }
 
 // ----------------------------------------------------------------------------------
