@@ -11,9 +11,16 @@
 // dense contraction on this path, so no MFMA.  The design points are
 //   * a lane owns 8 consecutive bf16 (one 16-byte load); a quad of lanes owns
 //     a 32-element MX block, so block reductions are two quad DPP steps;
-//   * one wavefront owns a whole row (hidden <= 4096) and keeps it in VGPRs
-//     between the row statistic and the cast -- one barrier (after the gain
-//     copy), at most 64 VGPRs, 8 waves per SIMD to keep HBM requests in flight;
+//   * one wavefront owns a whole row (hidden <= 2048, and rotated rows up to
+//     4096) and keeps it in VGPRs between the row statistic and the cast --
+//     one barrier (after the gain copy), at most 64 VGPRs, 8 waves per SIMD to
+//     keep HBM requests in flight;
+//   * wider rows are owned by 2, 4 or 8 waves, the two row reductions meeting
+//     in LDS; at 2048 < hidden <= 4096 without rotation 2 waves per row
+//     measured faster than one (16384 x 4096: 33.4 against 34.0 us; E2M1 27.7
+//     against 28.9 us): a wave's cast is half as long, and the cast of the
+//     rows that arrive last is what the launch waits for at its end (with H16
+//     one wave per row stays faster);
 //   * x is loaded and the codes stored non-temporally (each byte is touched
 //     once); the gain comes from L2, staged once per workgroup in LDS by
 //     LDS-DMA loads (wide rows: requested into VGPRs once the row has arrived);
@@ -344,9 +351,10 @@ __global__ __launch_bounds__(kThreads) void k_stream_pattern(const uint8_t* __re
 }
 
 // ----------------------------------------------------------------------------------
-// MXNorm forward for wide rows (4096 < hidden <= 32768): a row is owned by W
-// waves (4/W rows per workgroup); the two row reductions cross waves through
-// LDS.  Lane `lane` of wave `wir` owns chunk (s*W + wir)*64 + lane at step s.
+// MXNorm forward with a row owned by W waves (4/W rows per workgroup): 2048 <
+// hidden <= 4096 without rotation, and 4096 < hidden <= 32768; the two row
+// reductions cross waves through LDS.  Lane `lane` of wave `wir` owns chunk
+// (s*W + wir)*64 + lane at step s.
 // ----------------------------------------------------------------------------------
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
 __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const WaveArgs a) {
@@ -358,9 +366,10 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   __shared__ int s_max[NW];
   __shared__ double s_sum[NW];
   __shared__ uint32_t s_sc[NW][STEPS * 4];  // each wave's scale bytes, 16 per step
+  __shared__ uint4 s_gain[GAMMA ? W * STEPS * kWave : 1];  // the row's gain, chunk c at c
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rslot = wave / W;
   const int wir = wave % W;
   const int64_t row = (int64_t)blockIdx.x * RPW + rslot;
@@ -368,6 +377,20 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   const int nchunk = a.hidden >> 3;
   const int K = a.hidden >> 5;
 
+  // The gain is staged in LDS by LDS-DMA loads issued ahead of the row loads
+  // (wave w copies chunk groups w, w + NW, ...; chunks past the row end read
+  // as zero and are never used); they have landed once the row has, before
+  // the statistic's first barrier.
+  if constexpr (GAMMA) {
+    const rsrc_t rg = row_rsrc(a.gamma, (uint32_t)a.hidden * 2u);
+#pragma unroll
+    for (int j = 0; j < W * STEPS / NW; ++j) {
+      const int grp = j * NW + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + grp * kWave * 16), 16,
+          (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
+    }
+  }
   const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
   uint4 v[STEPS];
   bool act[STEPS];
@@ -378,16 +401,6 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     act[s] = row_ok && ch < nchunk;
     choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
     v[s] = load_stream16(xrow + choff[s]);
-  }
-  // the gain is requested once the row's chunks have arrived and lands while
-  // the statistic (and its two barriers) runs
-  uint4 gr[GAMMA ? STEPS : 1];
-  if constexpr (GAMMA) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) gr[s] = *reinterpret_cast<const uint4*>(a.gamma + choff[s]);
-  } else {
-    gr[0] = make_uint4(0, 0, 0, 0);
   }
 
   int u[STEPS], mp[STEPS];
@@ -400,6 +413,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   }
   umax = wave_max_quads(umax);
   if (lane == 0) s_max[wave] = umax;
+  if constexpr (GAMMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the gain copies
   __syncthreads();
   int E1 = s_max[rslot * W];
 #pragma unroll
@@ -424,7 +438,8 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   for (int s = 0; s < STEPS; ++s) {
     if (!act[s]) continue;  // quad-uniform
     const int ch = (s * W + wir) * kWave + lane;
-    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(v[s], gr[GAMMA ? s : 0], rho, lane,
+    const uint4 gv = GAMMA ? s_gain[ch] : make_uint4(0, 0, 0, 0);
+    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(v[s], gv, rho, lane,
                                                      crow + (uint32_t)ch * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
@@ -651,7 +666,12 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   if (r.waves == 1 && r.steps == 1) return launch_wave<ELEM, GAMMA, HAD, SRC, 1>(m);
   if (r.waves == 1 && r.steps == 2) return launch_wave<ELEM, GAMMA, HAD, SRC, 2>(m);
   if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
-  if (r.waves == 1 && r.steps == 8) return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
+  if (r.waves == 1 && r.steps == 8) {
+    // 2048 < hidden <= 4096: 2 waves per row, except with a rotation (its
+    // longer cast per element runs faster one wave per row)
+    if constexpr (HAD == 0) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
+    return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
+  }
   if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
   if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
   // the table's 4 x 16 entry (rows above 16384) runs here as 8 waves of 8 steps,
