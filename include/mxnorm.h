@@ -284,9 +284,10 @@ const char *mxq_status_str(mxq_status s);
  * mxq_stream_pattern -- a measurement reference, not a step of the method:
  * moves the bytes of an E4M3 mxnorm_fwd call (reads x [rows, hidden] bf16;
  * writes rows x hidden code bytes, rows x hidden/32 scale bytes and rows fp32
- * values) with the same access pattern as mxnorm_fwd's one-wave-per-row
- * kernel (non-temporal 16-byte loads per lane, 8-byte code stores, one scale
- * dword per lane, one value per row), doing no arithmetic beyond an XOR fold
+ * values) with the access pattern of mxnorm_fwd's one-wave-per-row kernel
+ * (non-temporal 16-byte loads per lane, 8-byte code stores, one scale dword
+ * per lane, one value per row; mxnorm_fwd splits rows of 2048 < hidden <=
+ * 4096 over two waves, with the same lane chunks), doing no arithmetic beyond an XOR fold
  * of the loaded words into the stored ones.  Its run time is the practical
  * HBM ceiling of that byte pattern, against which the forward is compared.
  *   x : device, 16-byte aligned;  codes : 16-byte aligned;  scales, rrms :
