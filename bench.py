@@ -13,7 +13,8 @@ a roofline object for the kernel, the CPU oracle timed on the host as a
 reference baseline, and context figures (the two-pass RMSNorm + MX cast
 baseline, the straight-through backward on the same matrix, MXNormLinear
 (the MXFP8 matmul on the same matrix times a 4096 x 4096 folded weight), the
-other workloads, a rotated 1 GiB device copy).
+other workloads, the H32 / H16-to-E4M3 / exact-absmax variants, a rotated
+1 GiB device copy).
 
 `python bench.py --counters` only runs the headline kernel and a 256 MiB
 device copy (the calibration for HBM byte counters) for rocprofv3 --pmc;
@@ -450,6 +451,39 @@ def main():
             del sc
             torch.cuda.empty_cache()
         extras["other_workloads"] = others
+
+        # the variants beside the method's main path (context): H32 -> E2M1 and
+        # H16 -> E4M3 on workload 5's matrix, and the exact-absmax block
+        # magnitude (mxnorm_fwd_ex) on the headline matrix
+        variants = {}
+        xc, gc = W.workload_inputs(5)
+        r, d = xc.shape
+        for had, elem, name in ((32, mxq.E2M1, "h32_e2m1"), (16, mxq.E4M3, "h16_e4m3")):
+            gdev, sc = device_sets(xc, gc, elem, max(2, args.buffers // 2))
+            cl = mxnorm_calls(sc, gdev, r, d, 2, elem, had)
+            nst = max(30, args.steps // 4)
+            wl, gt = time_region(cl, nst, None)
+            b = algorithmic_bytes(r, d, elem)
+            variants["%s_%dx%d_p2" % (name, r, d)] = {
+                "kernel_us_mean": round(gt / nst * 1e6, 3),
+                "GBps_kernel": round(b * nst / gt / 1e9, 1)}
+            del sc
+            torch.cuda.empty_cache()
+        gdev, sc = device_sets(xb, gb, w.elem, max(2, args.buffers // 2))
+        cl = []
+        for s_ in sc:
+            a_ = (s_["x"].data_ptr(), gdev.data_ptr(), rows, hidden, 2, 0.0, mxq.SRC_ABSMAX, 0,
+                  w.elem, s_["codes"].data_ptr(), s_["scales"].data_ptr(), s_["rrms"].data_ptr(), sp)
+            cl.append(lambda a_=a_: L.mxnorm_fwd_ex(*a_))
+        nst = max(30, args.steps // 4)
+        wl, gt = time_region(cl, nst, None)
+        b = algorithmic_bytes(rows, hidden, w.elem)
+        variants["absmax_e4m3_%dx%d_p2" % (rows, hidden)] = {
+            "kernel_us_mean": round(gt / nst * 1e6, 3),
+            "GBps_kernel": round(b * nst / gt / 1e9, 1)}
+        del sc
+        torch.cuda.empty_cache()
+        extras["variants"] = variants
 
     # ------------------------------------------------------- CPU oracle baseline
     cpu = None
