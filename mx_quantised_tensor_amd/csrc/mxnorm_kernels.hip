@@ -23,7 +23,7 @@
 //     one wave per row stays faster);
 //   * x is loaded and the codes stored non-temporally (each byte is touched
 //     once); the gain comes from L2, staged once per workgroup in LDS by
-//     LDS-DMA loads (wide rows: requested into VGPRs once the row has arrived);
+//     LDS-DMA loads;
 //   * workgroups keep the hardware's round-robin spread over the 8 XCDs, so
 //     the whole chip sweeps one contiguous region of HBM at a time (giving
 //     each XCD its own contiguous range of rows measured ~5% slower).
@@ -274,9 +274,9 @@ __device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[ST
 // The gain is staged once per workgroup in LDS by gfx950's LDS-DMA buffer loads
 // (no VGPRs: 53 instead of 78 at hidden 4096, so 8 waves per SIMD instead of
 // 6, and a quarter of the gain's L2 reads), issued ahead of the row loads; one
-// barrier after they land.  Measured at 16384 x 4096 against requesting the
-// whole gain into VGPRs per wave: 34.0 against 34.6 us (H16 -> E2M1 at 32768
-// rows: 60.9 against 62.6 us).
+// barrier after they land.  Measured against requesting the whole gain into
+// VGPRs per wave, when this kernel still served 16384 x 4096 without rotation:
+// 34.0 against 34.6 us; H16 -> E2M1 at 32768 x 4096: 60.9 against 62.6 us.
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
