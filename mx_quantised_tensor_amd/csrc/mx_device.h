@@ -69,6 +69,12 @@ __device__ __forceinline__ int wave_max_quads(int v) {
   return max(max(a, b), max(c, d));
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ double dpp_f64_ror4(double v) {
   uint64_t u = __double_as_longlong(v);
   uint32_t lo = dpp_u32<kDppRowRor4>((uint32_t)u), hi = dpp_u32<kDppRowRor4>((uint32_t)(u >> 32));

@@ -317,6 +317,148 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
 }
 
 // ----------------------------------------------------------------------------------
+// MXNorm forward with the H32 rotation ([P3] "Metodologia") on rows of exactly
+// 4096, a lane owning whole 16-element groups: group g = t * 64 + lane at step
+// t (two 16-byte loads 16 bytes apart), so stages h = 1, 2, 4, 8 of the
+// transform run in-lane and only h = 16 crosses to the partner lane (lane ^ 1);
+// an MX block is a lane pair.  The butterflies are the same operations in the
+// same order as in k_mxnorm_wave, so the results are identical.  Measured on
+// 32768 x 4096 against one wave per row with 8-element chunks: H32 -> E2M1
+// 63.2 against 69.7 us, H32 -> E4M3 73.0 against 76.0 us; with H16 this layout
+// measured no faster (62.0 against 61.7 us; E4M3 72.2 against 69.2 us), so
+// H16 keeps the 8-element chunks.
+// ----------------------------------------------------------------------------------
+template <int ELEM, bool GAMMA, int HAD>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
+  constexpr int kHidden = 4096;
+  constexpr int T = kHidden / (16 * kWave);  // groups per lane
+  constexpr int K = kHidden / 32;
+  constexpr int EMAX = Elem<ELEM>::kEmax;
+  static_assert(HAD == 16 || HAD == 32, "rotation size");
+  __shared__ uint32_t s_sc[4][K / 4];  // each wave's scale bytes
+  __shared__ uint4 s_gain[GAMMA ? kHidden / 8 : 1];  // 8-element chunk c at c
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const bool row_ok = row < a.rows;  // waves past the end still copy the gain and meet the barrier
+  if constexpr (GAMMA) {
+    const rsrc_t rg = row_rsrc(a.gamma, kHidden * 2u);
+#pragma unroll
+    for (int j = 0; j < kHidden / 8 / kWave / 4; ++j) {
+      const int grp = j * 4 + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + grp * kWave * 16), 16,
+          (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
+    }
+  }
+  const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)(kHidden * 2);
+  uint4 v[2 * T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint32_t off = (uint32_t)(t * kWave + lane) * 32u;
+    v[2 * t] = load_stream16(xrow + off);
+    v[2 * t + 1] = load_stream16(xrow + off + 16u);
+  }
+  if constexpr (GAMMA) {
+    // the copies were issued before the 2T row loads
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * T) : "memory");
+    __syncthreads();
+  }
+  if (!row_ok) return;  // whole wave, after the only barrier
+
+  // block exponents (the E8M0 scales of x): the pair's two 16-element halves
+  int u[T];
+  int umax = kInactive;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    uint32_t m = max(absmax8_bf16_bits(v[2 * t]), absmax8_bf16_bits(v[2 * t + 1]));
+    m = max(m, dpp0_u32<kDppQuadSwap1>(m));
+    u[t] = max((int)(m >> 7), EMAX);
+    umax = max(umax, u[t]);
+  }
+  umax = max(umax, (int)dpp0_u32<kDppQuadSwap2>((uint32_t)umax));  // quad-uniform
+  const int E1 = wave_max_quads(umax);
+  float rho;
+  {
+    const PowerSum<kSrcScales> ps(E1, a.p_shift);
+    double S = 0.0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) S += ps.term(u[t], 1);
+    if (lane & 1) S = 0.0;  // a block is held by a lane pair: count it once
+    S += dpp_f64<kDppQuadSwap2>(S);  // the quad's two blocks (exact: integer-valued terms)
+    S = wave_sum_quads_f64(S);
+    rho = rho_from_stat<kSrcScales>(E1, S, a.p_shift, a.c, a.inv_k);
+  }
+  if (a.rrms != nullptr && lane == 0) a.rrms[row] = rho;
+
+  uint8_t* crow = a.codes + row * (int64_t)(ELEM == 0 ? kHidden : kHidden / 2);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int g = t * kWave + lane;
+    float lo[8], hi[8];  // elements 0..7 and 8..15 of the group
+    widen8(v[2 * t], lo);
+    widen8(v[2 * t + 1], hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = lo[i] * rho;
+      hi[i] = hi[i] * rho;
+    }
+    if constexpr (GAMMA) {
+      float g0[8], g1[8];
+      widen8(s_gain[2 * g], g0);
+      widen8(s_gain[2 * g + 1], g1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = lo[i] * g0[i];
+        hi[i] = hi[i] * g1[i];
+      }
+    }
+    fwht8_inlane(lo);  // h = 1, 2, 4 within each half
+    fwht8_inlane(hi);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // h = 8 across the halves
+      const float p = lo[j], q = hi[j];
+      lo[j] = p + q;
+      hi[j] = p - q;
+    }
+    if constexpr (HAD == 32) {  // h = 16 with the partner lane
+      fwht8_crosslane<kDppQuadSwap1>(lo, (lane & 1) != 0);
+      fwht8_crosslane<kDppQuadSwap1>(hi, (lane & 1) != 0);
+    }
+    constexpr float norm = HAD == 16 ? 0.25f : 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = lo[i] * norm;
+      hi[i] = hi[i] * norm;
+    }
+    uint32_t mb = max(absmax8_f32_bits(lo), absmax8_f32_bits(hi));
+    mb = max(mb, dpp0_u32<kDppQuadSwap1>(mb));
+    const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
+    if constexpr (ELEM == 0) {
+      const uint2 c0 = encode8_e4m3(lo, sb), c1 = encode8_e4m3(hi, sb);
+      const u32x4_t o = {c0.x, c0.y, c1.x, c1.y};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(crow + (uint32_t)g * 16u));
+    } else {
+      const u32x2_t o = {encode8_e2m1(lo, sb), encode8_e2m1(hi, sb)};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(crow + (uint32_t)g * 8u));
+    }
+    if (!(lane & 1)) reinterpret_cast<uint8_t*>(s_sc[wave])[t * 32 + (lane >> 1)] = (uint8_t)sb;
+  }
+  // the scale bytes written above are read back by other lanes of the wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint8_t* srow = a.scales + row * K;
+  if (a.scales_dwords) {
+    if (lane < K / 4) reinterpret_cast<uint32_t*>(srow)[lane] = s_sc[wave][lane];
+  } else {
+#pragma unroll
+    for (int j = 0; j < K / kWave; ++j)
+      srow[j * kWave + lane] = reinterpret_cast<const uint8_t*>(s_sc[wave])[j * kWave + lane];
+  }
+}
+
+// ----------------------------------------------------------------------------------
 // Measurement reference: the byte pattern of k_mxnorm_wave (E4M3, one wave per
 // row, the same lane layout, non-temporal loads and code stores, one scale
 // dword per lane, rho from lane 0) with no arithmetic but an XOR fold, whose
@@ -660,6 +802,15 @@ hipError_t launch_wide(const MxnormArgs& m) {
   return hipGetLastError();
 }
 
+template <int ELEM, bool GAMMA, int HAD>
+hipError_t launch_group16(const MxnormArgs& m) {
+  const WaveArgs a = wave_args(m);
+  const dim3 grid((unsigned)((m.rows + 3) / 4));
+  hipLaunchKernelGGL((k_mxnorm_group16<ELEM, GAMMA, HAD>), grid, dim3(kThreads), 0,
+                     (hipStream_t)m.stream, a);
+  return hipGetLastError();
+}
+
 template <int ELEM, bool GAMMA, int HAD, int SRC>
 hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   const RowShape r = pick_row_shape(m.hidden);
@@ -668,9 +819,16 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
   if (r.waves == 1 && r.steps == 8) {
     // 2048 < hidden <= 4096: 2 waves per row, except with a rotation (its
-    // longer cast per element runs faster one wave per row)
-    if constexpr (HAD == 0) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
-    return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
+    // longer cast per element runs faster one wave per row); H32 on rows of
+    // exactly 4096 with whole 16-groups per lane
+    if constexpr (HAD == 0) {
+      return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
+    } else {
+      if constexpr (HAD == 32 && SRC == kSrcScales) {
+        if (m.hidden == 4096) return launch_group16<ELEM, GAMMA, HAD>(m);
+      }
+      return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
+    }
   }
   if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
   if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
