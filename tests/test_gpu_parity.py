@@ -127,6 +127,35 @@ def test_mxnorm_ragged_row_counts(rows):
     _check_mxnorm(xb, gb, 2, C_DEF[2], 0, what="rows=%d" % rows)
 
 
+@pytest.mark.parametrize("hidden,had", [(4096, 0), (4096, 16), (4096, 32), (2048, 0), (8192, 0)])
+@pytest.mark.parametrize("elem", [0, 1])
+def test_mxnorm_scales_at_odd_address(hidden, had, elem):
+    """Scale bytes written one byte at a time when the scales buffer is not
+    4-byte aligned (every kernel has that path beside its dword stores)."""
+    rows = 13
+    xb, gb = W.generate(rows, hidden, "outlier", seed=hidden + had + elem)
+    x = P.to_device_bf16(xb)
+    g = P.to_device_bf16(gb)
+    k = hidden // 32
+    buf = torch.full((rows * k + 1,), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = buf[1:]
+    print("case: hidden=%d had=%d elem=%d scales at +1" % (hidden, had, elem), flush=True)
+    if had:
+        codes, _, rho = mxq.mxnorm_hadamard_fwd(x, g, p=2, c=C_DEF[2], had=had, elem=elem,
+                                                scales=scales)
+        oc, os_, orr = O.mxnorm_hadamard_fwd(xb, gb, 2, C_DEF[2], had, elem)
+    else:
+        codes, _, rho = mxq.mxnorm_fwd(x, g, p=2, c=C_DEF[2], elem=elem, scales=scales)
+        oc, os_, orr = O.mxnorm_fwd(xb, gb, 2, C_DEF[2], elem)
+    torch.cuda.synchronize()
+    what = "D=%d H%d elem=%d odd scales" % (hidden, had, elem)
+    assert int(buf[0].item()) == 0x5A, "byte before the scales was written"
+    gs = P.from_device(scales).reshape(rows, k)
+    P.assert_rho_equal(P.from_device(rho), orr, what)
+    P.assert_scales_equal(gs, os_, what)
+    P.assert_codes(P.from_device(codes), oc, os_, elem, exact=True, what=what)
+
+
 def _edge_rows(hidden):
     rng = np.random.default_rng(7)
     base = rng.standard_normal(hidden)
