@@ -267,6 +267,13 @@ def main():
         extras["headline_no_gain_algorithmic_GBps"] = round(
             algorithmic_bytes(rows, hidden, w.elem, gamma=False) / (gng / nng) / 1e9, 1)
         del ng_calls
+        # warm-cache context: one buffer set reused every step (x 128 MiB and
+        # its codes fit the 256 MB Infinity Cache together)
+        nwarm = max(30, args.steps // 4)
+        _, gwarm = time_region(calls[:1], nwarm, None)
+        extras["headline_one_buffer_set_us_per_call"] = round(gwarm / nwarm * 1e6, 3)
+        extras["headline_one_buffer_set_algorithmic_GBps"] = round(
+            algorithmic_bytes(rows, hidden, w.elem) / (gwarm / nwarm) / 1e9, 1)
         # two-pass baseline on the same workload
         del sets, calls
         torch.cuda.empty_cache()
