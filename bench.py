@@ -445,7 +445,7 @@ def main():
             xc, gc = W.workload_inputs(cfg)
             r, d = xc.shape
             nset = 2 if r * d <= 256 * 1024 else max(2, args.buffers // 2)
-            gdev, sc = device_sets(xc, gc, wc.elem, nset)
+            gdev, sc = device_sets(xc, gc, wc.elem, nset, two_pass=(cfg == 2))
             for p in wc.ps:
                 cl = mxnorm_calls(sc, gdev, r, d, p, wc.elem, wc.had)
                 nst = max(30, args.steps // 4)
@@ -455,6 +455,23 @@ def main():
                     "kernel_us_mean": round(gt / nst * 1e6, 3),
                     "GBps_kernel": round(b * nst / gt / 1e9, 1),
                     "GBps_wall": round(b * nst / wl / 1e9, 1)}
+            if cfg == 2:
+                # this workload is defined against the two-pass RMSNorm + MX cast
+                tp = []
+                for s_ in sc:
+                    a_ = (s_["x"].data_ptr(), gdev.data_ptr(), r, d, 1e-5, wc.elem,
+                          s_["y"].data_ptr(), s_["codes"].data_ptr(), s_["scales"].data_ptr(),
+                          s_["rrms"].data_ptr(), sp)
+                    tp.append(lambda a_=a_: L.rmsnorm_mxquant_fwd(*a_))
+                nst = max(30, args.steps // 4)
+                _, gt2 = time_region(tp, nst, None)
+                others["%s_two_pass" % wc.name] = {
+                    "kernel_us_mean": round(gt2 / nst * 1e6, 3),
+                    "GBps_kernel": round(two_pass_bytes(r, d, wc.elem) * nst / gt2 / 1e9, 1)}
+                for p in wc.ps:
+                    k = "%s_p%d" % (wc.name, p)
+                    others[k]["speedup_vs_two_pass"] = round(
+                        (gt2 / nst * 1e6) / others[k]["kernel_us_mean"], 3)
             del sc
             torch.cuda.empty_cache()
         extras["other_workloads"] = others
