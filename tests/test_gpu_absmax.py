@@ -60,6 +60,15 @@ def test_absmax_shapes(hidden, elem):
         _check(xb, None, p, 1.25, elem, what="D=%d p=%d no gamma" % (hidden, p))
 
 
+@pytest.mark.parametrize("had", [16, 32])
+@pytest.mark.parametrize("hidden", [3072, 4096])
+@pytest.mark.parametrize("elem", [0, 1])
+def test_absmax_with_rotation(had, hidden, elem):
+    xb, gb = W.generate(29, hidden, "outlier", seed=had + hidden + elem)
+    _check(xb, gb, 2, C_ABS[2], elem, had=had, what="D=%d H%d absmax" % (hidden, had))
+    _check(xb, None, 1, 1.25, elem, had=had, what="D=%d H%d absmax no gamma" % (hidden, had))
+
+
 def _edge_rows(hidden):
     rng = np.random.default_rng(17)
     base = rng.standard_normal(hidden)
