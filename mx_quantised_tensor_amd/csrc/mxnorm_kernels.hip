@@ -317,18 +317,25 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
 }
 
 // ----------------------------------------------------------------------------------
-// MXNorm forward with the H32 rotation ([P3] "Metodologia") on rows of exactly
-// 4096, a lane owning whole 16-element groups: group g = t * 64 + lane at step
-// t (two 16-byte loads 16 bytes apart), so stages h = 1, 2, 4, 8 of the
-// transform run in-lane and only h = 16 crosses to the partner lane (lane ^ 1);
-// an MX block is a lane pair.  The butterflies are the same operations in the
-// same order as in k_mxnorm_wave, so the results are identical.  Measured on
-// 32768 x 4096 against one wave per row with 8-element chunks: H32 -> E2M1
-// 63.2 against 69.7 us, H32 -> E4M3 73.0 against 76.0 us; with H16 this layout
-// measured no faster (62.0 against 61.7 us; E4M3 72.2 against 69.2 us), so
-// H16 keeps the 8-element chunks.
+// MXNorm forward with a rotation ([P3] "Metodologia") on rows of exactly 4096,
+// a lane owning whole 16-element groups, so stages h = 1, 2, 4, 8 of the
+// transform run in-lane (and for H32 only h = 16 crosses lanes).  The
+// butterflies are the same operations in the same order as in k_mxnorm_wave,
+// so the results are identical.  Two ways to get the groups into lanes:
+//   * EXCH = false: group g = t * 64 + lane at step t, two 16-byte loads 16
+//     bytes apart; an MX block is the lane pair (l, l ^ 1);
+//   * EXCH = true: contiguous 1 KiB loads of chunks t*128 + lane and
+//     t*128 + 64 + lane, then partner lanes (l, l ^ 1) swap halves by DPP on
+//     the packed bf16 words: even lane 2m holds group t*64 + m, odd lane
+//     2m + 1 group t*64 + 32 + m; an MX block is the lane pair (l, l ^ 2).
+// Measured on 32768 x 4096 against one wave per row with 8-element chunks:
+// H32 -> E2M1 63.2 against 69.7 us and H32 -> E4M3 73.0 against 76.0 us with
+// EXCH = false (EXCH = true: 64.3 us); H16 with gain -> E2M1 60.1 against
+// 61.3 us and -> E4M3 66.2 against 68.9 us with EXCH = true (EXCH = false: no
+// faster), but H16 without gain 60.8 against 59.7 us, so only H16 with a gain
+// runs here.
 // ----------------------------------------------------------------------------------
-template <int ELEM, bool GAMMA, int HAD>
+template <int ELEM, bool GAMMA, int HAD, bool EXCH>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
   constexpr int kHidden = 4096;
   constexpr int T = kHidden / (16 * kWave);  // groups per lane
@@ -351,13 +358,24 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
           (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
     }
   }
+  // DPP control reaching the lane that holds the other group of the lane's MX
+  // block, and the one reaching the quad's other block
+  constexpr int kBlk = EXCH ? kDppQuadSwap2 : kDppQuadSwap1;
+  constexpr int kQuad = EXCH ? kDppQuadSwap1 : kDppQuadSwap2;
+  const int blk_bit = EXCH ? 2 : 1;  // lane bit telling the block's upper group
+  const bool even = (lane & 1) == 0;
   const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)(kHidden * 2);
   uint4 v[2 * T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const uint32_t off = (uint32_t)(t * kWave + lane) * 32u;
-    v[2 * t] = load_stream16(xrow + off);
-    v[2 * t + 1] = load_stream16(xrow + off + 16u);
+    if constexpr (EXCH) {
+      v[2 * t] = load_stream16(xrow + (uint32_t)(t * 2 * kWave + lane) * 16u);
+      v[2 * t + 1] = load_stream16(xrow + (uint32_t)(t * 2 * kWave + kWave + lane) * 16u);
+    } else {
+      const uint32_t off = (uint32_t)(t * kWave + lane) * 32u;
+      v[2 * t] = load_stream16(xrow + off);
+      v[2 * t + 1] = load_stream16(xrow + off + 16u);
+    }
   }
   if constexpr (GAMMA) {
     // the copies were issued before the 2T row loads
@@ -365,6 +383,23 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
     __syncthreads();
   }
   if (!row_ok) return;  // whole wave, after the only barrier
+  if constexpr (EXCH) {
+    // even lane: keeps chunk A (group t*64 + m, first half), takes the odd
+    // partner's A (second half); odd lane: keeps B (group t*64 + 32 + m,
+    // second half), takes the even partner's B (first half)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint4 A = v[2 * t], B = v[2 * t + 1];
+      const uint4 snd = even ? B : A;
+      uint4 rcv;
+      rcv.x = dpp_u32<kDppQuadSwap1>(snd.x);
+      rcv.y = dpp_u32<kDppQuadSwap1>(snd.y);
+      rcv.z = dpp_u32<kDppQuadSwap1>(snd.z);
+      rcv.w = dpp_u32<kDppQuadSwap1>(snd.w);
+      v[2 * t] = even ? A : rcv;
+      v[2 * t + 1] = even ? rcv : B;
+    }
+  }
 
   // block exponents (the E8M0 scales of x): the pair's two 16-element halves
   int u[T];
@@ -372,11 +407,11 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     uint32_t m = max(absmax8_bf16_bits(v[2 * t]), absmax8_bf16_bits(v[2 * t + 1]));
-    m = max(m, dpp0_u32<kDppQuadSwap1>(m));
+    m = max(m, dpp0_u32<kBlk>(m));
     u[t] = max((int)(m >> 7), EMAX);
     umax = max(umax, u[t]);
   }
-  umax = max(umax, (int)dpp0_u32<kDppQuadSwap2>((uint32_t)umax));  // quad-uniform
+  umax = max(umax, (int)dpp0_u32<kQuad>((uint32_t)umax));  // quad-uniform
   const int E1 = wave_max_quads(umax);
   float rho;
   {
@@ -384,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
     double S = 0.0;
 #pragma unroll
     for (int t = 0; t < T; ++t) S += ps.term(u[t], 1);
-    if (lane & 1) S = 0.0;  // a block is held by a lane pair: count it once
-    S += dpp_f64<kDppQuadSwap2>(S);  // the quad's two blocks (exact: integer-valued terms)
+    if (lane & blk_bit) S = 0.0;  // a block is held by a lane pair: count it once
+    S += dpp_f64<kQuad>(S);  // the quad's two blocks (exact: integer-valued terms)
     S = wave_sum_quads_f64(S);
     rho = rho_from_stat<kSrcScales>(E1, S, a.p_shift, a.c, a.inv_k);
   }
@@ -394,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
   uint8_t* crow = a.codes + row * (int64_t)(ELEM == 0 ? kHidden : kHidden / 2);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int g = t * kWave + lane;
+    const int g = EXCH ? t * kWave + (lane >> 1) + (even ? 0 : kWave / 2) : t * kWave + lane;
     float lo[8], hi[8];  // elements 0..7 and 8..15 of the group
     widen8(v[2 * t], lo);
     widen8(v[2 * t + 1], hi);
@@ -421,9 +456,9 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
       lo[j] = p + q;
       hi[j] = p - q;
     }
-    if constexpr (HAD == 32) {  // h = 16 with the partner lane
-      fwht8_crosslane<kDppQuadSwap1>(lo, (lane & 1) != 0);
-      fwht8_crosslane<kDppQuadSwap1>(hi, (lane & 1) != 0);
+    if constexpr (HAD == 32) {  // h = 16 with the lane holding the block's other group
+      fwht8_crosslane<kBlk>(lo, (lane & blk_bit) != 0);
+      fwht8_crosslane<kBlk>(hi, (lane & blk_bit) != 0);
     }
     constexpr float norm = HAD == 16 ? 0.25f : 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
 #pragma unroll
@@ -432,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
       hi[i] = hi[i] * norm;
     }
     uint32_t mb = max(absmax8_f32_bits(lo), absmax8_f32_bits(hi));
-    mb = max(mb, dpp0_u32<kDppQuadSwap1>(mb));
+    mb = max(mb, dpp0_u32<kBlk>(mb));
     const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
     if constexpr (ELEM == 0) {
       const uint2 c0 = encode8_e4m3(lo, sb), c1 = encode8_e4m3(hi, sb);
@@ -442,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
       const u32x2_t o = {encode8_e2m1(lo, sb), encode8_e2m1(hi, sb)};
       __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(crow + (uint32_t)g * 8u));
     }
-    if (!(lane & 1)) reinterpret_cast<uint8_t*>(s_sc[wave])[t * 32 + (lane >> 1)] = (uint8_t)sb;
+    if (!(lane & blk_bit)) reinterpret_cast<uint8_t*>(s_sc[wave])[g >> 1] = (uint8_t)sb;
   }
   // the scale bytes written above are read back by other lanes of the wave
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -802,11 +837,11 @@ hipError_t launch_wide(const MxnormArgs& m) {
   return hipGetLastError();
 }
 
-template <int ELEM, bool GAMMA, int HAD>
+template <int ELEM, bool GAMMA, int HAD, bool EXCH>
 hipError_t launch_group16(const MxnormArgs& m) {
   const WaveArgs a = wave_args(m);
   const dim3 grid((unsigned)((m.rows + 3) / 4));
-  hipLaunchKernelGGL((k_mxnorm_group16<ELEM, GAMMA, HAD>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((k_mxnorm_group16<ELEM, GAMMA, HAD, EXCH>), grid, dim3(kThreads), 0,
                      (hipStream_t)m.stream, a);
   return hipGetLastError();
 }
@@ -819,13 +854,13 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
   if (r.waves == 1 && r.steps == 8) {
     // 2048 < hidden <= 4096: 2 waves per row, except with a rotation (its
-    // longer cast per element runs faster one wave per row); H32 on rows of
-    // exactly 4096 with whole 16-groups per lane
+    // longer cast per element runs faster one wave per row); H32, and H16
+    // with a gain, on rows of exactly 4096 with whole 16-groups per lane
     if constexpr (HAD == 0) {
       return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
     } else {
-      if constexpr (HAD == 32 && SRC == kSrcScales) {
-        if (m.hidden == 4096) return launch_group16<ELEM, GAMMA, HAD>(m);
+      if constexpr (SRC == kSrcScales && (HAD == 32 || GAMMA)) {
+        if (m.hidden == 4096) return launch_group16<ELEM, GAMMA, HAD, HAD == 16>(m);
       }
       return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
     }
