@@ -245,9 +245,10 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  *               bytes, 16-byte aligned, caller-owned; required iff gamma !=
  *               NULL and rows > 0; its contents on entry do not matter
  * hidden must be a multiple of 32 and at most MXQ_MAX_HIDDEN (MXQ_EUNSUPPORTED
- * above).  The sum over a row of x.g: per-lane fused multiply-add chains of
- * 64 products, a fixed tree over the wave, and for rows wider than 4096 the
- * 2, 4 or 8 wave sums added in wave order.
+ * above).  The sum over a row of x.g: per-lane fused multiply-add chains over
+ * the lane's 8-element chunks in order, a fixed tree over the wave, and where
+ * a row is split over 2, 4 or 8 waves (rows wider than 4096; without a gain,
+ * rows wider than 2048) the wave sums added in wave order.
  * Two launches with a gain (rows, then the dgamma column sums), one without.
  */
 mxq_status mxnorm_bwd(const void *x, const void *dy, const void *gamma, const float *rrms,

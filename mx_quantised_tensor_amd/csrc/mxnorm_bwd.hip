@@ -24,8 +24,10 @@
 //     writes one partial row; a second kernel adds the partial rows column
 //     by column in a fixed order.  Both orders depend only on (rows, hidden),
 //     so results are run-to-run reproducible;
-//   * without a gain every wave takes one row (four per workgroup), as in the
-//     forward;
+//   * without a gain every wave takes one row (four per workgroup) up to
+//     hidden 2048; above that a row is split over 2 waves (as in the forward:
+//     measured at 16384 x 4096, 64.3 against 66.3 us with one wave per row --
+//     a wave's share of the last rows' work is half as long);
 //   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
 //     workgroup of W waves), lane `lane` of wave `wir` holding chunk
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
@@ -251,11 +253,11 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
   }
 }
 
-// Rows of 4096 < hidden <= 4096 W: a workgroup of W waves owns one row at a
-// time (8 chunks per lane).
-template <bool GAMMA, int W, bool FULL>
+// Rows of up to 512 W STEPS elements: a workgroup of W waves owns one row at a
+// time (STEPS chunks per lane): 4096 < hidden <= 4096 W with 8 steps, and
+// without a gain 2048 < hidden <= 4096 with 2 waves of 4 steps.
+template <bool GAMMA, int W, bool FULL, int STEPS = 8>
 __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
-  constexpr int STEPS = 8;
   const int lane = threadIdx.x & 63;
   const int wir = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nchunk = a.hidden >> 3;
@@ -386,14 +388,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, int groups, void* stream) {
   return hipGetLastError();
 }
 
-template <bool GAMMA, int W>
+template <bool GAMMA, int W, int STEPS = 8>
 hipError_t launch_bwd_wide_t(const BwdArgs& a, int groups, void* stream) {
-  if (a.hidden == 4096 * W)
-    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, true>), dim3(groups), dim3(W * 64), 0,
+  if (a.hidden == 512 * STEPS * W)
+    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, true, STEPS>), dim3(groups), dim3(W * 64), 0,
                        (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, false>), dim3(groups), dim3(W * 64), 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((k_mxnorm_bwd_wide<GAMMA, W, false, STEPS>), dim3(groups), dim3(W * 64),
+                       0, (hipStream_t)stream, a);
   return hipGetLastError();
 }
 
@@ -402,6 +404,9 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
   if (a.hidden > 16384) return launch_bwd_wide_t<GAMMA, 8>(a, groups, stream);
   if (a.hidden > 8192) return launch_bwd_wide_t<GAMMA, 4>(a, groups, stream);
   if (a.hidden > 4096) return launch_bwd_wide_t<GAMMA, 2>(a, groups, stream);
+  if constexpr (!GAMMA) {
+    if (a.hidden > 2048) return launch_bwd_wide_t<GAMMA, 2, 4>(a, groups, stream);
+  }
   const int nchunk = a.hidden / 8;
   if (nchunk <= 64) return launch_bwd_t<GAMMA, 1>(a, groups, stream);
   if (nchunk <= 128) return launch_bwd_t<GAMMA, 2>(a, groups, stream);
@@ -439,9 +444,10 @@ hipError_t launch_mxnorm_bwd(const BwdLaunch& l) {
   a.dx = static_cast<uint8_t*>(l.dx);
   a.partial = l.workspace;
   // with a gain the workgroups are persistent (one dgamma partial row each);
-  // without one every wave takes a single row, as in the forward
+  // without one a row takes one wave up to hidden 2048 (four rows per
+  // workgroup) and a workgroup of 2 or more waves above
   const int groups = (int)(l.gamma ? bwd_groups(l.rows, l.hidden)
-                          : bwd_waves_per_row(l.hidden) == 1 ? (l.rows + 3) / 4 : l.rows);
+                          : l.hidden <= 2048 ? (l.rows + 3) / 4 : l.rows);
   if (groups > 0) {
     const hipError_t e = l.gamma ? launch_bwd_steps<true>(a, groups, l.stream)
                                  : launch_bwd_steps<false>(a, groups, l.stream);
