@@ -254,7 +254,7 @@ def test_baseline_workload2_full():
     _check_baseline(xb, gb, 1e-5, 0, "two-pass C2")
 
 
-@pytest.mark.parametrize("hidden", [32, 96, 768, 4096, 4128, 16384])
+@pytest.mark.parametrize("hidden", [32, 96, 768, 3104, 4096, 4128, 16384])
 @pytest.mark.parametrize("elem", [0, 1])
 def test_baseline_shapes(hidden, elem):
     xb, gb = W.generate(33, hidden, "rowscale", seed=hidden + 11)
