@@ -332,8 +332,8 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
 // H32 -> E2M1 63.2 against 69.7 us and H32 -> E4M3 73.0 against 76.0 us with
 // EXCH = false (EXCH = true: 64.3 us); H16 with gain -> E2M1 60.1 against
 // 61.3 us and -> E4M3 66.2 against 68.9 us with EXCH = true (EXCH = false: no
-// faster), but H16 without gain 60.8 against 59.7 us, so only H16 with a gain
-// runs here.
+// faster), but H16 without gain 60.8 against 59.7 us: H32 runs here with
+// EXCH = false, H16 with a gain with EXCH = true, H16 without one does not.
 // ----------------------------------------------------------------------------------
 template <int ELEM, bool GAMMA, int HAD, bool EXCH>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
