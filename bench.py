@@ -18,7 +18,8 @@ other workloads, the H32 / H16-to-E4M3 / exact-absmax variants, a rotated
 
 `python bench.py --counters` only runs the headline kernel and a 256 MiB
 device copy (the calibration for HBM byte counters) for rocprofv3 --pmc;
-`python bench.py --counters-matmul` only runs the 16384 x 4096 x 4096 MXFP8
+`python bench.py --counters-h16` does the same for the 32768 x 4096 H16 -> E2M1
+forward; `python bench.py --counters-matmul` only runs the 16384 x 4096 x 4096 MXFP8
 matmul (5 launches), for the matrix kernel's counters.
 """
 import argparse
@@ -98,6 +99,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--counters", action="store_true",
                     help="run only the headline kernel and a calibration copy (for --pmc)")
+    ap.add_argument("--counters-h16", action="store_true",
+                    help="run only the 32768x4096 H16 -> E2M1 forward (20 times) and a "
+                         "calibration copy (for --pmc)")
     ap.add_argument("--counters-matmul", action="store_true",
                     help="run only the 16384x4096x4096 MXFP8 matmul, 5 times (for --pmc)")
     args = ap.parse_args()
@@ -200,6 +204,19 @@ def main():
     w = W.WORKLOADS[HEADLINE]
     xb, gb = W.workload_inputs(HEADLINE)
     rows, hidden = xb.shape
+    if args.counters_h16:
+        w5 = W.WORKLOADS[5]
+        x5, g5 = W.workload_inputs(5)
+        r5, d5 = x5.shape
+        gdev5, s5 = device_sets(x5, g5, w5.elem, 2)
+        run(mxnorm_calls(s5, gdev5, r5, d5, 2, w5.elem, w5.had), 20)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("counters run: 20 x mxnorm_hadamard_fwd %dx%d H16 E2M1, 20 x 256 MiB copy" % (r5, d5))
+        return
     if args.counters_matmul:
         xt = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         xc, xs = mxq.mxnorm_fwd(xt, None, p=2)[:2]
