@@ -531,7 +531,9 @@ __global__ __launch_bounds__(kThreads) void k_stream_pattern(const uint8_t* __re
 // MXNorm forward with a row owned by W waves (4/W rows per workgroup): 2048 <
 // hidden <= 4096 without rotation, and 4096 < hidden <= 32768; the two row
 // reductions cross waves through LDS.  Lane `lane` of wave `wir` owns chunk
-// (s*W + wir)*64 + lane at step s.
+// (wir*STEPS + s)*64 + lane at step s: each wave streams its own contiguous
+// part of the row (measured 0.6-1.4% faster at 8192 and 32768 than waves
+// interleaving 1 KiB steps, the same at 4096).
 // ----------------------------------------------------------------------------------
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
 __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const WaveArgs a) {
@@ -574,7 +576,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   uint32_t choff[STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int ch = (s * W + wir) * kWave + lane;
+    const int ch = (wir * STEPS + s) * kWave + lane;
     act[s] = row_ok && ch < nchunk;
     choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
     v[s] = load_stream16(xrow + choff[s]);
@@ -614,13 +616,13 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     if (!act[s]) continue;  // quad-uniform
-    const int ch = (s * W + wir) * kWave + lane;
+    const int ch = (wir * STEPS + s) * kWave + lane;
     const uint4 gv = GAMMA ? s_gain[ch] : make_uint4(0, 0, 0, 0);
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(v[s], gv, rho, lane,
                                                      crow + (uint32_t)ch * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
-  // Step s of this wave covers blocks (s W + wir) * 16 .. + 15 of the row: 16
+  // Step s of this wave covers blocks (wir STEPS + s) * 16 .. + 15 of the row: 16
   // scale bytes gathered in LDS, written as four dwords (or bytes when the
   // row's scales are not dword-aligned).  Other lanes of the wave read them.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -629,7 +631,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   if (a.scales_dwords) {
     const int s = lane >> 2, q = lane & 3;  // step, dword within the step
     if (s < STEPS && row_ok) {
-      const int b0 = (s * W + wir) * 16;  // first block of the step
+      const int b0 = (wir * STEPS + s) * 16;  // first block of the step
       if (b0 + 4 * q < K) reinterpret_cast<uint32_t*>(srow + b0)[q] = s_sc[wave][s * 4 + q];
     }
   } else {
@@ -637,7 +639,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     for (int j = 0; j < (STEPS * 16 + kWave - 1) / kWave; ++j) {
       const int i = j * kWave + lane;  // byte i of this wave's gathered scales
       const int s = i >> 4;
-      const int blk = (s * W + wir) * 16 + (i & 15);
+      const int blk = (wir * STEPS + s) * 16 + (i & 15);
       if (s < STEPS && row_ok && blk < K)
         srow[blk] = reinterpret_cast<const uint8_t*>(s_sc[wave])[i];
     }
