@@ -193,6 +193,24 @@ def test_mxnorm_default_c_and_optional_rrms():
     P.assert_codes(P.from_device(c1), oc, os_, 0)
 
 
+@pytest.mark.parametrize("hidden,had", [(2048, 0), (4096, 16), (4096, 32), (8192, 0)])
+def test_optional_rrms_every_kernel(hidden, had):
+    """Without a rho output every kernel the launcher picks writes the same codes
+    and scales."""
+    xb, gb = W.generate(37, hidden, "outlier", seed=hidden + had)
+    x, g = P.to_device_bf16(xb), P.to_device_bf16(gb)
+    if had:
+        c1, s1, r1 = mxq.mxnorm_hadamard_fwd(x, g, p=2, c=0.0, had=had, elem=mxq.E2M1)
+        c2, s2, r2 = mxq.mxnorm_hadamard_fwd(x, g, p=2, c=0.0, had=had, elem=mxq.E2M1,
+                                             want_rrms=False)
+    else:
+        c1, s1, r1 = mxq.mxnorm_fwd(x, g, p=2, c=0.0)
+        c2, s2, r2 = mxq.mxnorm_fwd(x, g, p=2, c=0.0, want_rrms=False)
+    torch.cuda.synchronize()
+    assert r2 is None and r1 is not None
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+
+
 def test_mxnorm_deterministic_and_side_stream():
     xb, gb = W.workload_inputs(2)
     x, g = P.to_device_bf16(xb), P.to_device_bf16(gb)
