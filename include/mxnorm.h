@@ -231,8 +231,10 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  * g = dy * gamma (g = dy without a gain), per row:
  *     dx_j     = rho * g_j - rho^3 * x_j * (1/hidden) * sum_k x_k g_k
  *     dgamma_j = sum over rows of dy_j * x_j * rho
- * computed in fp32 (sum_k x_k g_k: per-lane FMA chains, then a fixed tree)
- * and dx rounded to bf16 (nearest even).  dgamma is summed in an order that
+ * computed in fp32 as dx_j = rho * (g_j - y_j * m) with y = fl(rho * x) and
+ * m = (1/hidden) * sum_k y_k g_k (the same value; no intermediate overflows
+ * unless dx does), and dx rounded to bf16 (nearest even); dgamma_j
+ * accumulates fma(dy_j * x_j, rho, .).  dgamma is summed in an order that
  * depends only on (rows, hidden): results are bit-reproducible run to run.
  *   x, dy     : device bf16 [rows, hidden] (the forward's input and the
  *               gradient of its output), 16-byte aligned
@@ -245,7 +247,7 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  *               bytes, 16-byte aligned, caller-owned; required iff gamma !=
  *               NULL and rows > 0; its contents on entry do not matter
  * hidden must be a multiple of 32 and at most MXQ_MAX_HIDDEN (MXQ_EUNSUPPORTED
- * above).  The sum over a row of x.g: per-lane fused multiply-add chains over
+ * above).  The sum over a row of y.g: per-lane fused multiply-add chains over
  * the lane's 8-element chunks in order, a fixed tree over the wave, and where
  * a row is split over 2, 4 or 8 waves (rows wider than 4096; without a gain,
  * rows wider than 2048) the wave sums added in wave order.

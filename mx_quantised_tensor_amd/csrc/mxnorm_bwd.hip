@@ -8,6 +8,11 @@
 // with g = dy * gamma
 //     dx_j     = rho * g_j - rho^3 * x_j * (1/D) sum_k x_k g_k
 //     dgamma_j = sum over rows of dy_j * x_j * rho.
+// dx is evaluated as rho * (g_j - y_j * m), y = rho * x (the normalised row,
+// |y| < 2 c K^(1/p)) and m = (1/D) sum_k y_k g_k: no intermediate overflows
+// unless dx itself does (rho^3 alone overflows fp32 once rho > 2^42, e.g. for
+// an all-zero row, whose rho is c * 2^(127 - emax)), and the products summed
+// stay clear of fp32 subnormals for rows of tiny magnitude.
 //
 // Like the forward, this is an HBM-bound streaming pass (read x and dy, write
 // dx: 6 bytes per element); no dense contraction, no MFMA.
@@ -31,7 +36,7 @@
 //   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
 //     workgroup of W waves), lane `lane` of wave `wir` holding chunk
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
-//     of x.g are added through LDS in wave order.  With a gain the workgroups
+//     of y.g are added through LDS in wave order.  With a gain the workgroups
 //     are persistent over rows (512 of 2 waves, 256 of 4 or 8 waves: measured
 //     best); each wave owns distinct columns, so it writes its part of the
 //     workgroup's partial row directly.
@@ -97,7 +102,7 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, int64_t row, const ui
 
 // dx of one row (and its dgamma contribution added to acc).  W > 1: the row is
 // shared by the W waves of the workgroup; s_dot (2 W floats, alternating
-// halves by row parity `par`) carries their partial sums of x.g.
+// halves by row parity `par`) carries their partial sums of y.g.
 template <bool GAMMA, int STEPS, int W = 1>
 __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
                                         const uint32_t (&choff)[STEPS], const bool (&act)[STEPS],
@@ -108,7 +113,8 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
   // never waits for vector loads issued after this row's
   const float rho = ((const __attribute__((address_space(4))) float*)a.rrms)[row];
 
-  // s = sum_k x_k g_k (fp32; per-lane FMA chain, then a fixed wave tree)
+  // sum_k y_k g_k with y_k = fl(rho x_k) (fp32; per-lane FMA chain, then a
+  // fixed wave tree)
   float dot = 0.0f;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
@@ -123,7 +129,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
       for (int i = 0; i < 8; ++i) g[i] = g[i] * gf[i];  // exact: 8-bit x 8-bit significands
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(xf[i], g[i], dot);
+    for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(xf[i] * rho, g[i], dot);
   }
   dot = wave_sum_f32(dot);
   if constexpr (W > 1) {
@@ -143,7 +149,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
   for (int s = 0; s < STEPS; ++s)
     __asm__ volatile("" : "+v"(xv[s].x), "+v"(xv[s].y), "+v"(xv[s].z), "+v"(xv[s].w),
                      "+v"(dv[s].x), "+v"(dv[s].y), "+v"(dv[s].z), "+v"(dv[s].w));
-  const float corr = ((rho * rho) * rho) * (dot * a.inv_d);
+  const float m = dot * a.inv_d;  // mean of y g
 
   uint8_t* drow = a.dx + row * (int64_t)a.hidden * 2;
 #pragma unroll
@@ -159,7 +165,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float g = GAMMA ? dyf[i] * gf[i] : dyf[i];
-      d[i] = __builtin_fmaf(-corr, xf[i], rho * g);
+      d[i] = rho * __builtin_fmaf(-m, xf[i] * rho, g);
       if constexpr (GAMMA) acc[s][i] = __builtin_fmaf(dyf[i] * xf[i], rho, acc[s][i]);
     }
     store_nt16(drow + choff[s], bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]),

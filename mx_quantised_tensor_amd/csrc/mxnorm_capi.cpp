@@ -48,6 +48,25 @@ mxq_status check_mx_outputs(const void* x, const uint8_t* codes, const uint8_t* 
 
 mxq_status status_of(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
 
+// Every argument check of mx_matmul (shapes, limits, pointers, alignment), so
+// that a composed call can run them all before its first launch.  MXQ_OK with
+// M == 0 or N == 0 means there is nothing to do.
+mxq_status check_matmul(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                        const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, const void* c,
+                        mxq_out c_type) {
+  if (M < 0 || N < 0 || K <= 0 || K % MXQ_BLOCK != 0) return MXQ_EINVAL;
+  if (c_type != MXQ_OUT_F32 && c_type != MXQ_OUT_BF16) return MXQ_EINVAL;
+  if (K % kMatmulK != 0 || K > MXQ_MAX_HIDDEN * 4) return MXQ_EUNSUPPORTED;
+  if (M > kMaxRows * 4 || N > kMaxRows * 4) return MXQ_EUNSUPPORTED;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 31)) return MXQ_EUNSUPPORTED;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MXQ_EINVAL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(c, 4))
+    return MXQ_EALIGN;
+  return MXQ_OK;
+}
+
 mxq_status mxnorm_common(const void* x, const void* gamma, int64_t rows, int64_t hidden, int p,
                          float c, mxq_source source, int had, mxq_elem elem, uint8_t* codes,
                          uint8_t* scales, float* rrms, mxq_stream_t stream) {
@@ -154,16 +173,8 @@ mxq_status mx_quant_gain(const void* w, const void* gamma, int64_t rows, int64_t
 mxq_status mx_matmul(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                      const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
                      mxq_out c_type, mxq_stream_t stream) {
-  if (M < 0 || N < 0 || K <= 0 || K % MXQ_BLOCK != 0) return MXQ_EINVAL;
-  if (c_type != MXQ_OUT_F32 && c_type != MXQ_OUT_BF16) return MXQ_EINVAL;
-  if (K % kMatmulK != 0 || K > MXQ_MAX_HIDDEN * 4) return MXQ_EUNSUPPORTED;
-  if (M > kMaxRows * 4 || N > kMaxRows * 4) return MXQ_EUNSUPPORTED;
-  if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 31)) return MXQ_EUNSUPPORTED;
-  if (M == 0 || N == 0) return MXQ_OK;
-  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MXQ_EINVAL;
-  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
-      !aligned(b_scales, 4) || !aligned(c, 4))
-    return MXQ_EALIGN;
+  const mxq_status st = check_matmul(a_codes, a_scales, b_codes, b_scales, M, N, K, c, c_type);
+  if (st != MXQ_OK || M == 0 || N == 0) return st;
   (void)hipGetLastError();
   return status_of(mxq::launch_mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, (int)K, c,
                                        c_type == MXQ_OUT_BF16, stream));
@@ -180,7 +191,14 @@ mxq_status mxnorm_linear_fwd(const void* x, int64_t rows, int64_t hidden, int p,
   if (out_features < 0) return MXQ_EINVAL;
   if (out_type != MXQ_OUT_F32 && out_type != MXQ_OUT_BF16) return MXQ_EINVAL;
   if (hidden % kMatmulK != 0) return MXQ_EUNSUPPORTED;
+  // the product's checks first: nothing is launched unless both calls are valid
+  st = check_matmul(x_codes, x_scales, w_codes, w_scales, rows, out_features, hidden, out,
+                    out_type);
+  if (st != MXQ_OK) return st;
   if (rows == 0 || out_features == 0) return MXQ_OK;
+  if (x == nullptr) return MXQ_EINVAL;
+  if (!aligned(x, 16)) return MXQ_EALIGN;
+  if (rrms != nullptr && !aligned(rrms, 4)) return MXQ_EALIGN;
   st = mxnorm_common(x, nullptr, rows, hidden, p, c, MXQ_SRC_SCALES, 0, MXQ_E4M3, x_codes,
                      x_scales, rrms, stream);
   if (st != MXQ_OK) return st;

@@ -302,6 +302,9 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
             (int)((uint32_t)(s * kWave + lane) * 16u), 0, 0, 0);
     }
   }
+  // The wait below counts on the gain copies being issued before the row
+  // loads; this compiler barrier keeps any row load from being moved above them.
+  if constexpr (GAMMA) asm volatile("" ::: "memory");
   const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
   uint4 v[STEPS];
 #pragma unroll
@@ -358,6 +361,9 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
           (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
     }
   }
+  // The wait after the row loads counts on the gain copies being issued
+  // first; this compiler barrier keeps any row load from being moved above them.
+  if constexpr (GAMMA) asm volatile("" ::: "memory");
   // DPP control reaching the lane that holds the other group of the lane's MX
   // block, and the one reaching the quad's other block
   constexpr int kBlk = EXCH ? kDppQuadSwap2 : kDppQuadSwap1;

@@ -72,12 +72,13 @@ def assert_rho_equal(got, want, what=""):
 
 
 # ------------------------------------------------------------ straight-through backward
-# dx is computed in fp32 and rounded to bf16; the oracle is fp64.  With
-# u = 2^-24 and T_j = rho |g_j| + rho^3 |x_j| sum_k |x_k g_k| / D (the sizes of
-# the two terms), the fp32 evaluation is within about 80 u T_j of the exact
-# value (the dot product's FMA chain and tree, five roundings of the
-# correction, the product and the final FMA); rounding to bf16 adds half a
-# bf16 ulp.  The bar allows one bf16 ulp of the exact value plus 2^-16 T_j.
+# dx is computed in fp32 as rho (g_j - y_j m), y = fl(rho x), m = fl(sum y g / D),
+# and rounded to bf16; the oracle is fp64.  With u = 2^-24 and
+# T_j = rho |g_j| + rho^3 |x_j| sum_k |x_k g_k| / D (the sizes of the two terms
+# of dx), the fp32 evaluation is within about 80 u T_j of the exact value (the
+# rounding of each y, the dot product's FMA chain, tree and wave sums, the
+# mean, the FMA and the product by rho); rounding to bf16 adds half a bf16
+# ulp.  The bar allows one bf16 ulp of the exact value plus 2^-16 T_j.
 # dgamma sums fp32 contributions over rows in chains of at most a few hundred
 # additions for the sizes tested: the bar is 2^-12 of sum |dy x rho|.
 

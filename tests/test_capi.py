@@ -237,6 +237,27 @@ def test_matmul_argument_checks():
                                None) == EINVAL
 
 
+def test_linear_fwd_checks_the_product_before_launching():
+    # every one of these has a valid activation side: the call must still fail
+    # before the norm's launch (on this host a launch would report MXQ_EHIP)
+    L = mxq.lib()
+    lf = lambda **kw: L.mxnorm_linear_fwd(
+        kw.get("x", A16), 4, 128, 2, 0.0, kw.get("wc", A16), kw.get("ws", A16),
+        kw.get("n", 8), kw.get("xc", A16), kw.get("xs", A16), None, kw.get("out", A16),
+        kw.get("t", 0), None)
+    assert lf(wc=None) == EINVAL
+    assert lf(ws=None) == EINVAL
+    assert lf(out=None) == EINVAL
+    assert lf(wc=MIS) == EALIGN
+    assert lf(ws=A16 + 2) == EALIGN
+    assert lf(xs=A16 + 2) == EALIGN      # the product reads x_scales as dwords
+    assert lf(out=A16 + 2) == EALIGN
+    assert lf(n=-1) == EINVAL
+    assert lf(n=1 << 27) == EUNSUP        # beyond the product's limits
+    assert lf(x=None) == EINVAL
+    assert lf(n=0, x=None, wc=None, ws=None, out=None) == OK
+
+
 def test_stream_pattern_argument_checks():
     L = mxq.lib()
     f = lambda **kw: L.mxq_stream_pattern(kw.get("x", A16), kw.get("rows", 4),

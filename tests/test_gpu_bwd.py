@@ -159,3 +159,25 @@ def test_bwd_maximum_rows_sampled():
     ref_dx, _ = O.mxnorm_bwd(xb, dyb, None, rho)
     got = dx[ti].view(torch.int16).cpu().numpy().view(np.uint16)
     P.assert_bwd_close(got, None, xb, dyb, None, rho, ref_dx, None, "bwd max rows")
+
+
+@pytest.mark.parametrize("with_gamma", [True, False])
+@pytest.mark.parametrize("hidden", [512, 4096, 8192, 32768])
+def test_bwd_zero_and_tiny_rows(hidden, with_gamma):
+    # an all-zero row (rho = c 2^119: rho^3 alone overflows fp32), an all -0 row,
+    # rows scaled by 2^-50 and 2^-120 (bf16 subnormals), between ordinary rows;
+    # every kernel shape: one wave per row, two waves, the wide persistent kernels
+    xb, gb = W.generate(6, hidden, "outlier", 61)
+    xv = P.bf16_bits_to_f64(xb)
+    xv[1] = 0.0
+    xv[2] *= 2.0 ** -50
+    xv[3] *= 2.0 ** -120
+    xb = W.to_bf16_bits(xv.astype(np.float32))
+    xb[4] = 0x8000
+    dyb = W.grad_output(6, hidden, 61)
+    _, _, rho = O.mxnorm_fwd(xb, gb, 2, C2, O.E4M3)
+    gb = gb if with_gamma else None
+    dxb, dg = _check(xb, dyb, gb, rho, "zero/tiny rows hidden=%d gamma=%s" % (hidden, with_gamma))
+    assert np.isfinite(P.bf16_bits_to_f64(dxb)).all()
+    if with_gamma:
+        assert np.isfinite(dg).all()

@@ -128,3 +128,41 @@ def test_zero_gradient_and_empty():
     assert not dx.any() and not dg.any()
     dx, dg = O.mxnorm_bwd(x[:0], dy[:0], g, rho[:0])
     assert dx.shape == (0, 512) and not dg.any()
+
+
+def tiny_rows(hidden, seed):
+    """Rows of the outlier generator, then: row 1 all zero (a padding token),
+    row 2 scaled by 2^-50, row 3 by 2^-120 (bf16 subnormal and near-subnormal
+    values), row 4 all -0."""
+    x, g = workloads.generate(6, hidden, "outlier", seed)
+    xv = f64(x)
+    xv[1] = 0.0
+    xv[2] *= 2.0 ** -50
+    xv[3] *= 2.0 ** -120
+    xb = bf16(xv)
+    xb[4] = 0x8000
+    dy = workloads.grad_output(6, hidden, seed)
+    _, _, rho = O.mxnorm_fwd(xb, g, 2, 1.7575276, O.E4M3)
+    return xb, dy, g, rho
+
+
+@pytest.mark.parametrize("with_gamma", [True, False])
+def test_zero_and_tiny_rows(with_gamma):
+    # The estimate of an all-zero row is c * 2^(127 - emax) (E4M3: ~1.76 * 2^119);
+    # RMSNorm's gradient there is rho * g (the correction term has a zero
+    # factor), which is finite; rows of tiny magnitude have a huge rho and
+    # still a gradient of ordinary size relative to rho * g.
+    x, dy, g, rho = tiny_rows(1024, 17)
+    g = g if with_gamma else None
+    assert rho[1] == np.float32(1.7575276 * 2.0 ** 119) and rho[4] == rho[1]
+    dx, dg = O.mxnorm_bwd(x, dy, g, rho)
+    assert np.isfinite(dx).all()
+    gv = f64(dy) if g is None else f64(dy) * f64(g)[None, :]
+    assert np.array_equal(dx[1], rho[1].astype(np.float64) * gv[1])
+    ref_dx, ref_dg = autograd_rmsnorm_at_rho(x, dy, g, rho)
+    err = np.abs(dx - ref_dx) / term_scale(x, dy, g, rho)
+    assert err.max() < 1e-12, err.max()
+    if with_gamma:
+        scale = np.sum(np.abs(f64(dy) * f64(x) * rho.astype(np.float64)[:, None]), axis=0)
+        assert np.isfinite(dg).all()
+        assert np.max(np.abs(dg - ref_dg) / scale) < 1e-12
