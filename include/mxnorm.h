@@ -264,6 +264,32 @@ mxq_status mxnorm_bwd(const void *x, const void *dy, const void *gamma, const fl
 size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 
 /*
+ * mxnorm_bwd_noalloc -- mxnorm_bwd for callers that cannot allocate device
+ * memory (work under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, kernels and results as mxnorm_bwd
+ * (bit-identical), without the workspace argument: the dgamma partial rows
+ * go to a static device array of mxnorm_bwd_noalloc_scratch_bytes() bytes
+ * (32 MiB) that each GPU the library runs on holds until the process ends.
+ * The call allocates and frees nothing.
+ *   - Shapes whose workspace (mxnorm_bwd_workspace_bytes) would exceed the
+ *     array return MXQ_EUNSUPPORTED (no supported shape does at present).
+ *   - `stream` must belong to the current device (MXQ_EINVAL otherwise);
+ *     the first call with a gain on a device looks up the array's device
+ *     address (MXQ_EHIP if that fails).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap
+ *     on a GPU (other streams, other host threads) race and give wrong
+ *     dgamma.  Calls ordered on one stream are safe; nothing needs clearing
+ *     between them (every partial row is written before it is read).
+ */
+mxq_status mxnorm_bwd_noalloc(const void *x, const void *dy, const void *gamma,
+                              const float *rrms, int64_t rows, int64_t hidden, void *dx,
+                              float *dgamma, mxq_stream_t stream);
+
+/* mxnorm_bwd_noalloc_scratch_bytes -- host function: size of the static
+ * scratch array of mxnorm_bwd_noalloc, per GPU, in bytes. */
+size_t mxnorm_bwd_noalloc_scratch_bytes(void);
+
+/*
  * mxnorm_default_c -- host function.  Default c(p, 32) for power-of-two block
  * magnitudes and Gaussian activations with a log-uniform row scale (the
  * pages call the constant precalculated but print no value; [P1] §2

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = ["E4M3", "E2M1", "BLOCK", "MAX_HIDDEN", "MxqError", "lib", "mx_quant", "mxnorm_fwd",
-           "mxnorm_bwd", "mxnorm_bwd_workspace_bytes", "mxnorm_fwd_ex", "SRC_SCALES",
+           "mxnorm_bwd", "mxnorm_bwd_workspace_bytes", "mxnorm_bwd_noalloc", "mxnorm_fwd_ex", "SRC_SCALES",
            "SRC_ABSMAX", "OUT_F32", "OUT_BF16", "mx_quant_gain", "mx_matmul", "mxnorm_linear_fwd",
            "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd", "mxnorm_default_c", "status_str",
            "library_path"]
@@ -67,6 +67,10 @@ def lib():
         L.mxnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
         L.mxnorm_bwd_workspace_bytes.restype = C.c_size_t
         L.mxnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+        L.mxnorm_bwd_noalloc.restype = i32
+        L.mxnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp]
+        L.mxnorm_bwd_noalloc_scratch_bytes.restype = C.c_size_t
+        L.mxnorm_bwd_noalloc_scratch_bytes.argtypes = []
         L.mx_quant_gain.restype = i32
         L.mx_quant_gain.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
         L.mx_matmul.restype = i32
@@ -246,6 +250,31 @@ def mxnorm_bwd(x, dy, rrms, gamma=None, dx=None, dgamma=None, workspace=None, st
         dgamma = None
     _check(lib().mxnorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(rrms), rows, hidden, _ptr(dx),
                             _ptr(dgamma), _ptr(workspace), _stream(stream)), "mxnorm_bwd")
+    return dx, dgamma
+
+
+def mxnorm_bwd_noalloc(x, dy, rrms, gamma=None, dx=None, dgamma=None, stream=None):
+    """mxnorm_bwd with the library's static per-GPU scratch instead of a
+    workspace (the C call allocates nothing; pass dx / dgamma to allocate
+    nothing here either).  Calls overlapping on one GPU race."""
+    x = _bf16_2d(x)
+    dy = _bf16_2d(dy)
+    rows, hidden = x.shape
+    if tuple(dy.shape) != (rows, hidden):
+        raise ValueError("dy must have the shape of x")
+    if rrms.dtype != torch.float32 or rrms.numel() != rows or not rrms.is_cuda:
+        raise ValueError("rrms must be a device fp32 tensor with one value per row")
+    gamma = _gamma(gamma, hidden)
+    if dx is None:
+        dx = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device)
+    if gamma is not None:
+        if dgamma is None:
+            dgamma = torch.empty((hidden,), dtype=torch.float32, device=x.device)
+    else:
+        dgamma = None
+    _check(lib().mxnorm_bwd_noalloc(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(rrms), rows, hidden,
+                                    _ptr(dx), _ptr(dgamma), _stream(stream)),
+           "mxnorm_bwd_noalloc")
     return dx, dgamma
 
 

@@ -67,4 +67,11 @@ int bwd_waves_per_row(int hidden);
 int64_t bwd_groups(int64_t rows, int hidden);
 hipError_t launch_mxnorm_bwd(const BwdLaunch& l);
 
+// Scratch of the allocation-free backward: a static device array of this many
+// bytes per GPU (the largest workspace any supported shape needs: 256 partial
+// rows of 32768 columns).  bwd_scratch returns its device address on `device`,
+// which must be the current device; the address is looked up once per device.
+constexpr size_t kBwdScratchBytes = (size_t)32 << 20;
+hipError_t bwd_scratch(int device, float** out);
+
 }  // namespace mxq

@@ -43,6 +43,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
 #include "mx_device.h"
 
@@ -421,6 +424,39 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
 }
 
 }  // namespace
+
+// The allocation-free backward's workspace: the dgamma partial rows live in
+// this array, which every GPU the library runs on holds until the process
+// ends.  In host code its name is only a stand-in for the symbol, not a device
+// address: kernels get the address hipGetSymbolAddress returns, looked up once
+// per device with that device current.  Every partial row a launch reads is
+// written by the same launch first, so nothing has to be cleared between calls.
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t bwd_scratch(int device, float** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_addr[device].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[device].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (addr == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(addr);
+      g_scratch_addr[device].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 int bwd_waves_per_row(int hidden) {
   return hidden > 16384 ? 8 : hidden > 8192 ? 4 : hidden > 4096 ? 2 : 1;

@@ -213,23 +213,40 @@ size_t mxnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
   return (size_t)mxq::bwd_groups(rows, (int)hidden) * (size_t)hidden * sizeof(float);
 }
 
-mxq_status mxnorm_bwd(const void* x, const void* dy, const void* gamma, const float* rrms,
-                      int64_t rows, int64_t hidden, void* dx, float* dgamma, float* workspace,
-                      mxq_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// mxnorm_bwd's argument checks; the workspace is checked only if `check_ws`.
+mxq_status check_bwd(const void* x, const void* dy, const void* gamma, const float* rrms,
+                     int64_t rows, int64_t hidden, const void* dx, const float* dgamma,
+                     bool check_ws, const float* workspace) {
   if (rows < 0 || hidden <= 0 || hidden % MXQ_BLOCK != 0) return MXQ_EINVAL;
   if (hidden > mxq::kBwdMaxHidden || rows > kMaxRows || rows > kMaxElems / hidden)
     return MXQ_EUNSUPPORTED;
   if (gamma != nullptr) {
-    if (dgamma == nullptr || (rows > 0 && workspace == nullptr)) return MXQ_EINVAL;
-    if (!aligned(gamma, 16) || !aligned(dgamma, 4) || !aligned(workspace, 16)) return MXQ_EALIGN;
+    if (dgamma == nullptr || (check_ws && rows > 0 && workspace == nullptr)) return MXQ_EINVAL;
+    if (!aligned(gamma, 16) || !aligned(dgamma, 4) || (check_ws && !aligned(workspace, 16)))
+      return MXQ_EALIGN;
   }
   if (rows > 0) {
     if (x == nullptr || dy == nullptr || rrms == nullptr || dx == nullptr) return MXQ_EINVAL;
     if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(rrms, 4))
       return MXQ_EALIGN;
-  } else if (gamma == nullptr) {
-    return MXQ_OK;  // nothing to do
   }
+  return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxq_status mxnorm_bwd(const void* x, const void* dy, const void* gamma, const float* rrms,
+                      int64_t rows, int64_t hidden, void* dx, float* dgamma, float* workspace,
+                      mxq_stream_t stream) {
+  const mxq_status st = check_bwd(x, dy, gamma, rrms, rows, hidden, dx, dgamma, true, workspace);
+  if (st != MXQ_OK) return st;
+  if (rows == 0 && gamma == nullptr) return MXQ_OK;  // nothing to do
   mxq::BwdLaunch l;
   l.x = x;
   l.dy = dy;
@@ -244,6 +261,29 @@ mxq_status mxnorm_bwd(const void* x, const void* dy, const void* gamma, const fl
   (void)hipGetLastError();
   return status_of(mxq::launch_mxnorm_bwd(l));
 }
+
+mxq_status mxnorm_bwd_noalloc(const void* x, const void* dy, const void* gamma, const float* rrms,
+                              int64_t rows, int64_t hidden, void* dx, float* dgamma,
+                              mxq_stream_t stream) {
+  mxq_status st = check_bwd(x, dy, gamma, rrms, rows, hidden, dx, dgamma, false, nullptr);
+  if (st != MXQ_OK) return st;
+  float* ws = nullptr;
+  if (gamma != nullptr && rows > 0) {
+    if (mxnorm_bwd_workspace_bytes(rows, hidden) > mxq::kBwdScratchBytes) return MXQ_EUNSUPPORTED;
+    // the scratch of the device the work runs on, which must be the current one
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXQ_EHIP;
+    if (stream != nullptr) {
+      hipDevice_t sdev = -1;
+      if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return MXQ_EHIP;
+      if ((int)sdev != dev) return MXQ_EINVAL;
+    }
+    if (mxq::bwd_scratch(dev, &ws) != hipSuccess) return MXQ_EHIP;
+  }
+  return mxnorm_bwd(x, dy, gamma, rrms, rows, hidden, dx, dgamma, ws, stream);
+}
+
+size_t mxnorm_bwd_noalloc_scratch_bytes(void) { return mxq::kBwdScratchBytes; }
 
 float mxnorm_default_c(int p) {
   if (p == 1) return kDefaultC1;

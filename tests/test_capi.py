@@ -270,3 +270,24 @@ def test_stream_pattern_argument_checks():
     assert f(x=None) == EINVAL
     assert f(x=MIS) == EALIGN
     assert f(scales=A16 + 2) == EALIGN
+
+
+def test_bwd_noalloc_argument_checks_and_scratch_size():
+    L = mxq.lib()
+    f = lambda **kw: L.mxnorm_bwd_noalloc(
+        kw.get("x", A16), kw.get("dy", A16), kw.get("g", A16), kw.get("r", A16),
+        kw.get("rows", 4), kw.get("hidden", 256), kw.get("dx", A16), kw.get("dg", A16), None)
+    assert f(rows=-1) == EINVAL
+    assert f(hidden=48) == EINVAL
+    assert f(hidden=32768 + 32) == EUNSUP
+    assert f(dg=None) == EINVAL          # a gain needs dgamma
+    assert f(x=None) == EINVAL
+    assert f(x=MIS) == EALIGN
+    assert f(g=MIS) == EALIGN
+    assert f(dg=A16 + 2) == EALIGN
+    assert f(rows=0, g=None, x=None, dy=None, r=None, dx=None, dg=None) == OK
+    # the static scratch covers the workspace of every supported shape
+    cap = L.mxnorm_bwd_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    need = max(mxq.mxnorm_bwd_workspace_bytes((1 << 24) - 1, h) for h in range(32, 32769, 32))
+    assert 0 < need <= cap
