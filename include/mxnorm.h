@@ -309,23 +309,6 @@ float mxnorm_default_c_for(int p, mxq_source source);
 /* mxq_status_str -- host function: a static, human-readable status name. */
 const char *mxq_status_str(mxq_status s);
 
-/*
- * mxq_stream_pattern -- a measurement reference, not a step of the method:
- * moves the bytes of an E4M3 mxnorm_fwd call (reads x [rows, hidden] bf16;
- * writes rows x hidden code bytes, rows x hidden/32 scale bytes and rows fp32
- * values) with the access pattern of mxnorm_fwd's one-wave-per-row kernel
- * (non-temporal 16-byte loads per lane, 8-byte code stores, one scale dword
- * per lane, one value per row; mxnorm_fwd splits rows of 2048 < hidden <=
- * 4096 over two waves, with the same lane chunks), doing no arithmetic beyond an XOR fold
- * of the loaded words into the stored ones.  Its run time is the practical
- * HBM ceiling of that byte pattern, against which the forward is compared.
- *   x : device, 16-byte aligned;  codes : 16-byte aligned;  scales, rrms :
- *   4-byte aligned.  hidden must be 512, 1024, 2048 or 4096 (else
- *   MXQ_EUNSUPPORTED).  The outputs hold no meaningful values.
- */
-mxq_status mxq_stream_pattern(const void *x, int64_t rows, int64_t hidden, uint8_t *codes,
-                              uint8_t *scales, float *rrms, mxq_stream_t stream);
-
 /* mxq_version -- host function: library version string. */
 const char *mxq_version(void);
 

@@ -84,8 +84,6 @@ def lib():
         L.mxnorm_default_c_for.argtypes = [i32, i32]
         L.mxnorm_default_c.restype = f32
         L.mxnorm_default_c.argtypes = [i32]
-        L.mxq_stream_pattern.restype = i32
-        L.mxq_stream_pattern.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.mxq_status_str.restype = C.c_char_p
         L.mxq_status_str.argtypes = [i32]
         L.mxq_version.restype = C.c_char_p

@@ -1,6 +1,7 @@
-"""Build libmxnorm.so (the C ABI + gfx950 HIP kernels) in-tree with hipcc.
+"""Build libmxnorm.so (the C ABI + gfx950 HIP kernels) in-tree with hipcc,
+and libmxq_measure.so (the benchmark's byte-pattern references).
 
-Output: mx_quantised_tensor_amd/lib/libmxnorm.so.  Flags:
+Output: mx_quantised_tensor_amd/lib/libmxnorm.so and libmxq_measure.so.  Flags:
   * --offload-arch=gfx950: MI355X code objects only;
   * -ffp-contract=off: no implicit FMA, every product and sum rounds once,
     as the method's fp32 steps are defined;
@@ -18,6 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmxnorm.so")
 SOURCES = ["mxnorm_kernels.hip", "mxnorm_bwd.hip", "mx_gemm.hip", "mxnorm_capi.cpp"]
+MEASURE_LIB = os.path.join(LIB_DIR, "libmxq_measure.so")
+MEASURE_SOURCES = ["measure.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -31,9 +34,16 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Build both libraries; returns the path of libmxnorm.so."""
+    _link(SOURCES, LIB, verbose)
+    _link(MEASURE_SOURCES, MEASURE_LIB, verbose)
+    return LIB
+
+
+def _link(sources, lib, verbose):
     os.makedirs(LIB_DIR, exist_ok=True)
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(LIB_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -46,13 +56,12 @@ def build(verbose: bool = False) -> str:
         if verbose and err.strip():
             print(err, flush=True)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     for o in objs:
         os.remove(o)
-    return LIB
 
 
 if __name__ == "__main__":

@@ -34,10 +34,6 @@ hipError_t launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int hi
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                           const uint8_t* bs, int64_t M, int64_t N, int K, void* c, bool c_bf16,
                           void* stream);
-// Measurement reference with the E4M3 one-wave-per-row forward's byte pattern
-// (hidden 512, 1024, 2048 or 4096).
-hipError_t launch_stream_pattern(const void* x, int64_t rows, int hidden, uint8_t* codes,
-                                 uint8_t* scales, float* rrms, void* stream);
 // MX cast of fl32(w * gamma) along rows of w (the gain folded into a weight).
 hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,
                                 int elem, uint8_t* codes, uint8_t* scales, void* stream);

@@ -310,20 +310,6 @@ const char* mxq_status_str(mxq_status s) {
   return "MXQ_UNKNOWN";
 }
 
-mxq_status mxq_stream_pattern(const void* x, int64_t rows, int64_t hidden, uint8_t* codes,
-                              uint8_t* scales, float* rrms, mxq_stream_t stream) {
-  if (rows < 0 || hidden <= 0) return MXQ_EINVAL;
-  if (hidden != 512 && hidden != 1024 && hidden != 2048 && hidden != 4096)
-    return MXQ_EUNSUPPORTED;
-  if (rows > kMaxRows) return MXQ_EUNSUPPORTED;
-  if (rows == 0) return MXQ_OK;
-  if (x == nullptr || codes == nullptr || scales == nullptr || rrms == nullptr) return MXQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(rrms, 4))
-    return MXQ_EALIGN;
-  (void)hipGetLastError();
-  return status_of(mxq::launch_stream_pattern(x, rows, (int)hidden, codes, scales, rrms, stream));
-}
-
 const char* mxq_version(void) { return "mxnorm-gfx950 0.1.0"; }
 
 }  // extern "C"

@@ -91,9 +91,11 @@ __device__ __forceinline__ void store_codes_stream(uint8_t* __restrict__ dst, co
 constexpr int kSrcScales = 0;
 constexpr int kSrcAbsmax = 1;
 
+// m: the lane's largest 15-bit magnitude pattern (bf16 bits of |x|), before
+// the quad maximum.
 template <int SRC, int EMAX>
-__device__ __forceinline__ int block_u(const uint4 v, int& mp, int p_shift) {
-  const uint32_t m = quad_max_u32(absmax8_bf16_bits(v));
+__device__ __forceinline__ int block_u_from(uint32_t m, int& mp, int p_shift) {
+  m = quad_max_u32(m);
   const int f = (int)(m >> 7);
   if constexpr (SRC == kSrcScales) {
     (void)p_shift;
@@ -104,6 +106,16 @@ __device__ __forceinline__ int block_u(const uint4 v, int& mp, int p_shift) {
     mp = p_shift ? M * M : M;
     return max(f, 1);
   }
+}
+
+// The lane's 8 values either as packed bf16 (the 15-bit magnitudes come from
+// the bit patterns) or already widened to fp32 (the magnitude of the largest
+// |x|, an exact bf16 value, is the top half of its fp32 pattern: v_maximum3
+// with |.| modifiers, 4 instructions instead of 8 on the packed words; NaN and
+// Inf keep exponent field 255).
+__device__ __forceinline__ uint32_t lane_mag(const uint4 v) { return absmax8_bf16_bits(v); }
+__device__ __forceinline__ uint32_t lane_mag(const float (&x)[8]) {
+  return absmax8_f32_bits(x) >> 16;
 }
 
 // The terms of the exact power sum, as doubles built from their exponent:
@@ -159,13 +171,12 @@ __device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, fl
 // ([P1] §2 "Implementacion": scale the values and produce the quantisation
 // scales in the same pass; [P3]: H16 / H32 rotation before the MXFP4 cast.)
 template <int ELEM, bool GAMMA, int HAD>
-__device__ __forceinline__ uint32_t cast_chunk(const uint4 xv, const uint4 gv, float rho,
+__device__ __forceinline__ uint32_t cast_chunk(const float (&x)[8], const uint4 gv, float rho,
                                                int lane, uint8_t* __restrict__ dst) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   float y[8];
-  widen8(xv, y);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = y[i] * rho;
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * rho;
   if constexpr (GAMMA) {
     float g[8];
     widen8(gv, g);
@@ -204,6 +215,33 @@ struct WaveArgs {
   int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
 };
 
+// Rows of up to 4 chunks per lane are widened to fp32 once, before the row
+// statistic, and kept (32 VGPRs at 4 chunks); with 8 chunks per lane the
+// statistic reads the packed words and the cast widens them.
+template <int STEPS>
+struct RowRegs {
+  static constexpr bool kWiden = STEPS <= 4;
+  float xf[kWiden ? STEPS : 1][8];
+  __device__ __forceinline__ void widen(const uint4 (&v)[STEPS]) {
+    if constexpr (kWiden) {
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) widen8(v[s], xf[s]);
+    }
+  }
+  __device__ __forceinline__ uint32_t mag(const uint4 (&v)[STEPS], int s) const {
+    if constexpr (kWiden) return lane_mag(xf[s]);
+    else return lane_mag(v[s]);
+  }
+  __device__ __forceinline__ void values(const uint4 (&v)[STEPS], int s, float (&out)[8]) const {
+    if constexpr (kWiden) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = xf[s][i];
+    } else {
+      widen8(v[s], out);
+    }
+  }
+};
+
 // The whole forward of one row held in VGPRs (v: the row; s_gain: the gain,
 // staged in LDS, chunk s * 64 + lane at index s * 64 + lane).
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
@@ -213,11 +251,13 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   const int K = a.hidden >> 5;
+  RowRegs<STEPS> rr;
+  rr.widen(v);
   int u[STEPS], mp[STEPS];
   int umax = kInactive;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    int us = block_u<SRC, EMAX>(v[s], mp[s], a.p_shift);
+    int us = block_u_from<SRC, EMAX>(rr.mag(v, s), mp[s], a.p_shift);
     if constexpr (!FULL) us = act[s] ? us : kInactive;
     u[s] = us;
     umax = max(umax, us);
@@ -240,8 +280,10 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
   for (int s = 0; s < STEPS; ++s) {
     if (!FULL && !act[s]) continue;  // quad-uniform; the DPP inside stays in the quad
     const uint4 gv = GAMMA ? s_gain[s * kWave + lane] : make_uint4(0, 0, 0, 0);
+    float x[8];
+    rr.values(v, s, x);
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(
-        v[s], gv, rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
+        x, gv, rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc)[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
   // the scale bytes written above are read back by other lanes of the wave
@@ -343,27 +385,28 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
   constexpr int kHidden = 4096;
   constexpr int T = kHidden / (16 * kWave);  // groups per lane
   constexpr int K = kHidden / 32;
+  constexpr int NG = kHidden / 16;           // 16-element groups per row
   constexpr int EMAX = Elem<ELEM>::kEmax;
   static_assert(HAD == 16 || HAD == 32, "rotation size");
   __shared__ uint32_t s_sc[4][K / 4];  // each wave's scale bytes
-  __shared__ uint4 s_gain[GAMMA ? kHidden / 8 : 1];  // 8-element chunk c at c
+  // The gain is widened to fp32 once per workgroup and staged in LDS, quarter
+  // q of group g (elements 4q .. 4q+3) at q * NG + g, so that the lanes of a
+  // wave read consecutive 16-byte slots (no bank conflicts); against bf16 in
+  // LDS this takes 16 widening instructions per group out of the cast, which
+  // these VALU-bound kernels pay for (workload 5: 58.4 against 59.9 us).
+  __shared__ float4 s_gainf[GAMMA ? kHidden / 4 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  const bool row_ok = row < a.rows;  // waves past the end still copy the gain and meet the barrier
+  const bool row_ok = row < a.rows;  // waves past the end still stage the gain and meet the barrier
+  uint4 graw[GAMMA ? kHidden / 8 / kThreads : 1];
   if constexpr (GAMMA) {
-    const rsrc_t rg = row_rsrc(a.gamma, kHidden * 2u);
+    // thread i loads 8-element chunks i and i + 256 (group c / 2, half c % 2)
 #pragma unroll
-    for (int j = 0; j < kHidden / 8 / kWave / 4; ++j) {
-      const int grp = j * 4 + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + grp * kWave * 16), 16,
-          (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
-    }
+    for (int j = 0; j < kHidden / 8 / kThreads; ++j)
+      graw[j] = reinterpret_cast<const uint4*>(a.gamma)[j * kThreads + threadIdx.x];
   }
-  // The wait after the row loads counts on the gain copies being issued
-  // first; this compiler barrier keeps any row load from being moved above them.
-  if constexpr (GAMMA) asm volatile("" ::: "memory");
+  if constexpr (GAMMA) asm volatile("" ::: "memory");  // keep the gain loads ahead of the row loads
   // DPP control reaching the lane that holds the other group of the lane's MX
   // block, and the one reaching the quad's other block
   constexpr int kBlk = EXCH ? kDppQuadSwap2 : kDppQuadSwap1;
@@ -379,13 +422,22 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
       v[2 * t + 1] = load_stream16(xrow + (uint32_t)(t * 2 * kWave + kWave + lane) * 16u);
     } else {
       const uint32_t off = (uint32_t)(t * kWave + lane) * 32u;
-      v[2 * t] = load_stream16(xrow + off);
-      v[2 * t + 1] = load_stream16(xrow + off + 16u);
+      // cached loads: the pair of 16-byte loads 16 bytes apart touches each
+      // line twice (measured 2% faster than non-temporal loads for H32)
+      v[2 * t] = *reinterpret_cast<const uint4*>(xrow + off);
+      v[2 * t + 1] = *reinterpret_cast<const uint4*>(xrow + off + 16u);
     }
   }
   if constexpr (GAMMA) {
-    // the copies were issued before the 2T row loads
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * T) : "memory");
+#pragma unroll
+    for (int j = 0; j < kHidden / 8 / kThreads; ++j) {
+      const int c = j * kThreads + threadIdx.x;
+      float f[8];
+      widen8(graw[j], f);
+      const int q = 2 * (c & 1);
+      s_gainf[q * NG + (c >> 1)] = make_float4(f[0], f[1], f[2], f[3]);
+      s_gainf[(q + 1) * NG + (c >> 1)] = make_float4(f[4], f[5], f[6], f[7]);
+    }
     __syncthreads();
   }
   if (!row_ok) return;  // whole wave, after the only barrier
@@ -446,8 +498,12 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
     }
     if constexpr (GAMMA) {
       float g0[8], g1[8];
-      widen8(s_gain[2 * g], g0);
-      widen8(s_gain[2 * g + 1], g1);
+      const float4 q0 = s_gainf[g], q1 = s_gainf[NG + g];
+      const float4 q2 = s_gainf[2 * NG + g], q3 = s_gainf[3 * NG + g];
+      g0[0] = q0.x; g0[1] = q0.y; g0[2] = q0.z; g0[3] = q0.w;
+      g0[4] = q1.x; g0[5] = q1.y; g0[6] = q1.z; g0[7] = q1.w;
+      g1[0] = q2.x; g1[1] = q2.y; g1[2] = q2.z; g1[3] = q2.w;
+      g1[4] = q3.x; g1[5] = q3.y; g1[6] = q3.z; g1[7] = q3.w;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         lo[i] = lo[i] * g0[i];
@@ -500,37 +556,154 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_group16(const WaveArgs a) {
 }
 
 // ----------------------------------------------------------------------------------
-// Measurement reference: the byte pattern of k_mxnorm_wave (E4M3, one wave per
-// row, the same lane layout, non-temporal loads and code stores, one scale
-// dword per lane, rho from lane 0) with no arithmetic but an XOR fold, whose
-// result every store carries so that, as in the real kernel, no store can
-// leave before the whole row has arrived.
+// MXNorm forward with a rotation ([P3] "Metodologia") then E2M1 on rows of
+// exactly 4096, a lane owning whole 32-element groups: group g = t*64 + lane at
+// step t (four 16-byte loads 16 bytes apart, cached, so the lines they share
+// are fetched once), which is one MX block, so every stage of the H32
+// transform (and of H16 on each half) runs in-lane and the block maxima need no
+// cross-lane step; its 16 code bytes are one 16-byte store.  Against
+// 16-element groups per lane this drops the cross-lane stage of H32 (a sign
+// flip and a DPP add per value) and the block pairs' DPP steps -- these
+// kernels are VALU-bound (H32 -> E2M1 with a gain: 863 against 977 VALU
+// instructions per row; 32768 x 4096: 59.1 against 62.3 us; H16 without a
+// gain 59.1 against 60.7 us).  With E4M3 codes (32 bytes per lane, two strided
+// stores) it measured slower (H16 -> E4M3: 73.5 against 66.4 us), so E4M3
+// keeps k_mxnorm_group16.  The butterflies are the same operations in the
+// same order, so the results are identical.  The gain is staged once per
+// workgroup as fp32, eighth e of group g (elements 4e .. 4e+3) at e * 128 + g,
+// so a wave's gain reads are consecutive 16-byte slots.
 // ----------------------------------------------------------------------------------
-template <int STEPS>
-__global__ __launch_bounds__(kThreads) void k_stream_pattern(const uint8_t* __restrict__ x,
-                                                             int64_t rows, int hidden,
-                                                             uint8_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales,
-                                                             float* __restrict__ rrms) {
+template <bool GAMMA, int HAD>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_lane32(const WaveArgs a) {
+  constexpr int kHidden = 4096;
+  constexpr int T = kHidden / (32 * kWave);  // 32-groups (MX blocks) per lane
+  constexpr int K = kHidden / 32;
+  constexpr int EMAX = Elem<1>::kEmax;
+  static_assert(HAD == 16 || HAD == 32, "rotation size");
+  __shared__ uint32_t s_sc[4][K / 4];  // each wave's scale bytes
+  __shared__ float4 s_gainf[GAMMA ? kHidden / 4 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= rows) return;
-  const uint8_t* xrow = x + row * (int64_t)hidden * 2;
-  uint4 v[STEPS];
+  const bool row_ok = row < a.rows;  // waves past the end still stage the gain and meet the barrier
+  uint4 graw[GAMMA ? kHidden / 8 / kThreads : 1];
+  if constexpr (GAMMA) {
+    // thread i loads 8-element chunks i and i + 256 (group c / 4, eighths
+    // 2 (c % 4) and 2 (c % 4) + 1)
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + (uint32_t)(s * kWave + lane) * 16u);
-  uint32_t f = 0;
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) f ^= v[s].x;
-  uint8_t* crow = codes + row * (int64_t)hidden;
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const u32x2_t o = {v[s].x ^ v[s].y ^ f, v[s].z ^ v[s].w};
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(crow + (uint32_t)(s * kWave + lane) * 8u));
+    for (int j = 0; j < kHidden / 8 / kThreads; ++j)
+      graw[j] = reinterpret_cast<const uint4*>(a.gamma)[j * kThreads + threadIdx.x];
+    asm volatile("" ::: "memory");  // keep the gain loads ahead of the row loads
   }
-  if (lane < (hidden >> 7)) reinterpret_cast<uint32_t*>(scales + row * (hidden >> 5))[lane] = f;
-  if (lane == 0) rrms[row] = __uint_as_float(f);
+  const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)(kHidden * 2);
+  uint4 v[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[t][i] = *reinterpret_cast<const uint4*>(xrow + (uint32_t)((t * kWave + lane) * 64 + i * 16));
+  if constexpr (GAMMA) {
+#pragma unroll
+    for (int j = 0; j < kHidden / 8 / kThreads; ++j) {
+      const int c = j * kThreads + threadIdx.x;
+      float f[8];
+      widen8(graw[j], f);
+      const int e = 2 * (c & 3);
+      s_gainf[e * (K) + (c >> 2)] = make_float4(f[0], f[1], f[2], f[3]);
+      s_gainf[(e + 1) * (K) + (c >> 2)] = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+  }
+  if (!row_ok) return;  // whole wave, after the only barrier
+
+  // block exponents (the E8M0 scales of x), one block per lane and step
+  int u[T];
+  int umax = kInactive;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint32_t m = max(max(absmax8_bf16_bits(v[t][0]), absmax8_bf16_bits(v[t][1])),
+                           max(absmax8_bf16_bits(v[t][2]), absmax8_bf16_bits(v[t][3])));
+    u[t] = max((int)(m >> 7), EMAX);
+    umax = max(umax, u[t]);
+  }
+  umax = max(umax, (int)dpp0_u32<kDppQuadSwap1>((uint32_t)umax));
+  umax = max(umax, (int)dpp0_u32<kDppQuadSwap2>((uint32_t)umax));  // quad-uniform
+  const int E1 = wave_max_quads(umax);
+  float rho;
+  {
+    const PowerSum<kSrcScales> ps(E1, a.p_shift);
+    double S = 0.0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) S += ps.term(u[t], 1);
+    S += dpp_f64<kDppQuadSwap1>(S);  // exact: integer-valued terms
+    S += dpp_f64<kDppQuadSwap2>(S);
+    S = wave_sum_quads_f64(S);
+    rho = rho_from_stat<kSrcScales>(E1, S, a.p_shift, a.c, a.inv_k);
+  }
+  if (a.rrms != nullptr && lane == 0) a.rrms[row] = rho;
+
+  uint8_t* crow = a.codes + row * (int64_t)(kHidden / 2);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int g = t * kWave + lane;
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f[8];
+      widen8(v[t][i], f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[8 * i + k] = f[k] * rho;
+    }
+    if constexpr (GAMMA) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 q = s_gainf[e * K + g];
+        y[4 * e] = y[4 * e] * q.x;
+        y[4 * e + 1] = y[4 * e + 1] * q.y;
+        y[4 * e + 2] = y[4 * e + 2] * q.z;
+        y[4 * e + 3] = y[4 * e + 3] * q.w;
+      }
+    }
+    // butterfly distances 1, 2, 4, 8 (each 16-element half), then 16 for H32
+#pragma unroll
+    for (int h = 1; h < HAD; h *= 2) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if ((j % (2 * h)) < h) {
+          const float p = y[j], q = y[j + h];
+          y[j] = p + q;
+          y[j + h] = p - q;
+        }
+      }
+    }
+    constexpr float norm = HAD == 16 ? 0.25f : 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = y[i] * norm;
+    float m8[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m8[i][k] = y[8 * i + k];
+    const uint32_t mb = max(max(absmax8_f32_bits(m8[0]), absmax8_f32_bits(m8[1])),
+                            max(absmax8_f32_bits(m8[2]), absmax8_f32_bits(m8[3])));
+    const uint32_t sb = e8m0_from_expfield<EMAX>(mb >> 23);
+    const u32x4_t o = {encode8_e2m1(m8[0], sb), encode8_e2m1(m8[1], sb),
+                       encode8_e2m1(m8[2], sb), encode8_e2m1(m8[3], sb)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(crow + (uint32_t)g * 16u));
+    reinterpret_cast<uint8_t*>(s_sc[wave])[g] = (uint8_t)sb;
+  }
+  // the scale bytes written above are read back by other lanes of the wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint8_t* srow = a.scales + row * K;
+  if (a.scales_dwords) {
+    if (lane < K / 4) reinterpret_cast<uint32_t*>(srow)[lane] = s_sc[wave][lane];
+  } else {
+#pragma unroll
+    for (int j = 0; j < K / kWave; ++j)
+      srow[j * kWave + lane] = reinterpret_cast<const uint8_t*>(s_sc[wave])[j * kWave + lane];
+  }
 }
 
 // ----------------------------------------------------------------------------------
@@ -588,11 +761,13 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     v[s] = load_stream16(xrow + choff[s]);
   }
 
+  RowRegs<STEPS> rr;
+  rr.widen(v);
   int u[STEPS], mp[STEPS];
   int umax = kInactive;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int us = block_u<SRC, EMAX>(v[s], mp[s], a.p_shift);
+    const int us = block_u_from<SRC, EMAX>(rr.mag(v, s), mp[s], a.p_shift);
     u[s] = act[s] ? us : kInactive;
     umax = max(umax, u[s]);
   }
@@ -624,7 +799,9 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     if (!act[s]) continue;  // quad-uniform
     const int ch = (wir * STEPS + s) * kWave + lane;
     const uint4 gv = GAMMA ? s_gain[ch] : make_uint4(0, 0, 0, 0);
-    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(v[s], gv, rho, lane,
+    float x[8];
+    rr.values(v, s, x);
+    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(x, gv, rho, lane,
                                                      crow + (uint32_t)ch * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
@@ -664,11 +841,10 @@ __global__ __launch_bounds__(kThreads) void k_mx_quant(const uint4* __restrict__
   constexpr int EMAX = Elem<ELEM>::kEmax;
   const int64_t ch = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (ch >= nchunks) return;  // nchunks % 4 == 0: quads stay whole
-  const uint4 v = x[ch];
-  const uint32_t m = quad_max_u32(absmax8_bf16_bits(v));
-  const uint32_t sb = e8m0_from_expfield<EMAX>(m >> 7);
   float y[8];
-  widen8(v, y);
+  widen8(x[ch], y);
+  const uint32_t m = quad_max_u32(lane_mag(y));
+  const uint32_t sb = e8m0_from_expfield<EMAX>(m >> 7);
   store_codes_stream<ELEM>(codes + ch * Elem<ELEM>::kCodeBytesPerLane, y, sb);
   if ((threadIdx.x & 3) == 0) scales[ch >> 2] = (uint8_t)sb;
 }
@@ -854,6 +1030,15 @@ hipError_t launch_group16(const MxnormArgs& m) {
   return hipGetLastError();
 }
 
+template <bool GAMMA, int HAD>
+hipError_t launch_lane32(const MxnormArgs& m) {
+  const WaveArgs a = wave_args(m);
+  const dim3 grid((unsigned)((m.rows + 3) / 4));
+  hipLaunchKernelGGL((k_mxnorm_lane32<GAMMA, HAD>), grid, dim3(kThreads), 0,
+                     (hipStream_t)m.stream, a);
+  return hipGetLastError();
+}
+
 template <int ELEM, bool GAMMA, int HAD, int SRC>
 hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   const RowShape r = pick_row_shape(m.hidden);
@@ -867,6 +1052,9 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
     if constexpr (HAD == 0) {
       return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
     } else {
+      if constexpr (SRC == kSrcScales && ELEM == 1) {
+        if (m.hidden == 4096) return launch_lane32<GAMMA, HAD>(m);
+      }
       if constexpr (SRC == kSrcScales && (HAD == 32 || GAMMA)) {
         if (m.hidden == 4096) return launch_group16<ELEM, GAMMA, HAD, HAD == 16>(m);
       }
@@ -936,21 +1124,6 @@ hipError_t launch_mxnorm(const MxnormArgs& a) {
   if (a.elem == 0)
     return a.gamma ? launch_mxnorm_had<0, true>(a) : launch_mxnorm_had<0, false>(a);
   return a.gamma ? launch_mxnorm_had<1, true>(a) : launch_mxnorm_had<1, false>(a);
-}
-
-hipError_t launch_stream_pattern(const void* x, int64_t rows, int hidden, uint8_t* codes,
-                                 uint8_t* scales, float* rrms, void* stream) {
-  const dim3 grid((unsigned)((rows + 3) / 4));
-  const uint8_t* xb = static_cast<const uint8_t*>(x);
-  hipStream_t st = (hipStream_t)stream;
-  switch (hidden) {
-    case 512: hipLaunchKernelGGL(k_stream_pattern<1>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
-    case 1024: hipLaunchKernelGGL(k_stream_pattern<2>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
-    case 2048: hipLaunchKernelGGL(k_stream_pattern<4>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
-    case 4096: hipLaunchKernelGGL(k_stream_pattern<8>, grid, dim3(kThreads), 0, st, xb, rows, hidden, codes, scales, rrms); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, int hidden,

@@ -258,12 +258,27 @@ def test_linear_fwd_checks_the_product_before_launching():
     assert lf(n=0, x=None, wc=None, ws=None, out=None) == OK
 
 
-def test_stream_pattern_argument_checks():
-    L = mxq.lib()
-    f = lambda **kw: L.mxq_stream_pattern(kw.get("x", A16), kw.get("rows", 4),
-                                          kw.get("hidden", 4096), kw.get("codes", A16),
-                                          kw.get("scales", A16), kw.get("rrms", A16), None)
+def test_measure_library_exports_and_checks():
+    # the benchmark's byte-pattern references live in their own library, so
+    # libmxnorm.so's C ABI holds only calls of the method
+    from mx_quantised_tensor_amd import measure
+    text = open(os.path.join(ROOT, "include", "mxq_measure.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, re.M))
+    assert names == {"mxq_pattern_supported", "mxq_measure_pattern"}
+    M = measure.lib()
+    for n in names:
+        assert hasattr(M, n), n
+    assert not hasattr(mxq.lib(), "mxq_stream_pattern")
+    sup = lambda lay, h: M.mxq_pattern_supported(lay, h)
+    assert sup(0, 4096) and sup(1, 4096) and sup(2, 4096) and sup(3, 4096) and sup(4, 4096)
+    assert sup(0, 512) and not sup(2, 512) and not sup(1, 512) and sup(1, 1024)
+    assert not sup(4, 1024) and sup(4, 2048) and not sup(0, 768) and not sup(5, 4096)
+    f = lambda **kw: M.mxq_measure_pattern(kw.get("lay", 0), kw.get("x", A16), kw.get("rows", 4),
+                                           kw.get("hidden", 4096), kw.get("codes", A16),
+                                           kw.get("scales", A16), kw.get("rrms", A16), None)
     assert f(hidden=768) == EUNSUP
+    assert f(lay=7) == EUNSUP
     assert f(hidden=0) == EINVAL
     assert f(rows=-1) == EINVAL
     assert f(rows=0, x=None) == OK

@@ -243,9 +243,14 @@ def test_hadamard_workload5_full():
 
 
 @pytest.mark.parametrize("had", [16, 32])
-def test_hadamard_edge_rows(had):
+@pytest.mark.parametrize("elem", [1, 0])
+def test_hadamard_edge_rows(had, elem):
+    # every rotation kernel at 4096 (a lane per 32-group for E2M1, per 16-group
+    # for E4M3 with a gain, one wave per row for H16 -> E4M3 without one)
     xb = _edge_rows(4096)
-    _check_mxnorm(xb, None, 2, 1.0, 1, had=had, what="H%d edge" % had)
+    gb = _bits(1 + 0.02 * np.random.default_rng(4).standard_normal(4096))
+    _check_mxnorm(xb, None, 2, 1.0, elem, had=had, what="H%d elem %d edge" % (had, elem))
+    _check_mxnorm(xb, gb, 2, C_DEF[2], elem, had=had, what="H%d elem %d edge gain" % (had, elem))
 
 
 # ----------------------------------------------------------- two-pass baseline
@@ -280,29 +285,36 @@ def test_baseline_shapes(hidden, elem):
     _check_baseline(xb, None, 0.0, elem, "two-pass D=%d no gamma" % hidden)
 
 
-def test_stream_pattern_reference_moves_the_bytes():
-    # the measurement reference reads every input word and writes every output
-    # byte of the forward's pattern: check its XOR fold on the host
-    rows, hidden = 37, 4096
-    rng = np.random.default_rng(99)
+@pytest.mark.parametrize("layout", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("hidden", [2048, 4096])
+def test_measure_patterns_move_the_bytes(layout, hidden):
+    # every byte-pattern reference reads every input word and writes every
+    # output byte of the forward's traffic: check its XOR outputs on the host
+    from mx_quantised_tensor_amd import measure
+    M = measure.lib()
+    if not M.mxq_pattern_supported(layout, hidden):
+        pytest.skip("layout %d does not cover hidden %d" % (layout, hidden))
+    rows = 37
+    rng = np.random.default_rng(99 + layout)
     xw = rng.integers(0, 2 ** 32, size=(rows, hidden // 2), dtype=np.uint32)
     x = torch.from_numpy(xw.view(np.int32)).cuda()
     codes = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
     scales = torch.empty((rows, hidden // 32), dtype=torch.uint8, device="cuda")
     rr = torch.empty((rows,), dtype=torch.float32, device="cuda")
-    st = mxq.lib().mxq_stream_pattern(x.data_ptr(), rows, hidden, codes.data_ptr(),
-                                      scales.data_ptr(), rr.data_ptr(), None)
+    print("case: pattern layout %d hidden %d" % (layout, hidden), flush=True)
+    st = M.mxq_measure_pattern(layout, x.data_ptr(), rows, hidden, codes.data_ptr(),
+                               scales.data_ptr(), rr.data_ptr(), None)
     assert st == 0
     torch.cuda.synchronize()
-    v = xw.reshape(rows, 8, 64, 4)                       # step, lane, word
-    f = np.bitwise_xor.reduce(v[:, :, :, 0], axis=1)     # [rows, lane]
-    lo = v[:, :, :, 0] ^ v[:, :, :, 1] ^ f[:, None, :]
-    hi = v[:, :, :, 2] ^ v[:, :, :, 3]
+    f = np.bitwise_xor.reduce(xw, axis=1)                 # [rows]
+    v = xw.reshape(rows, hidden // 8, 4)                  # 16-byte chunks
+    lo = v[:, :, 0] ^ v[:, :, 1] ^ f[:, None]
+    hi = v[:, :, 2] ^ v[:, :, 3]
     want = np.stack([lo, hi], axis=-1).reshape(rows, -1).view(np.uint8)
     assert np.array_equal(codes.cpu().numpy(), want)
     sw = scales.cpu().numpy().view(np.uint32)
-    assert np.array_equal(sw, f[:, :32])
-    assert np.array_equal(rr.cpu().numpy().view(np.uint32), f[:, 0])
+    assert np.array_equal(sw, np.repeat(f[:, None], hidden // 128, axis=1))
+    assert np.array_equal(rr.cpu().numpy().view(np.uint32), f)
 
 
 def test_mxnorm_maximum_rows_sampled():
