@@ -7,9 +7,11 @@ synthetic and resident in HBM before timing starts; R distinct input/output
 buffer sets are rotated so that the 256 MB Infinity Cache cannot serve a step
 from the previous one.  Before the W warm-up steps the same calls run for a
 fixed 0.1 s of GPU time, which brings the GPU from idle to its steady clocks
-(it needs ~30 ms of back-to-back work); then K steps are launched back to
-back through the C ABI on the current stream, one HIP event pair on that
-stream brackets them, and the wall clock between two synchronisations.
+(it needs ~30 ms of back-to-back work); then the K steps, captured as calls
+through the C ABI in one HIP graph, are replayed once on the current stream:
+one HIP event pair on that stream brackets the replay, and the wall clock
+between two synchronisations.  (The same K steps as direct calls are in
+`extras`.)
 
 Printed: one JSON line with the achieved algorithmic HBM throughput (GB/s),
 a roofline object for the kernel, the CPU oracle timed on the host as a
@@ -228,6 +230,31 @@ def main():
         wall = time.perf_counter() - t0
         return wall, e0.elapsed_time(e1) * 1e-3
 
+    def time_steps_graph(calls, steps, warmup):
+        """The timed region of the headline: clock ramp and `warmup` untimed
+        steps as direct calls, then the `steps` calls captured in one HIP graph
+        (capture runs nothing; one untimed replay uploads it), then one timed
+        replay: wall time between two synchronisations and GPU time from one
+        event pair on the replay stream."""
+        clock_ramp(calls)
+        run(calls, warmup)
+        gr = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(gr, stream=cap):
+            run(calls, steps, torch.cuda.current_stream().cuda_stream)
+        gr.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del gr
+        return wall, e0.elapsed_time(e1) * 1e-3
+
     def graph_us(calls, n=200, seconds=0.06):
         """Mean GPU time per call (us) of n calls captured in one HIP graph,
         replayed back to back for ~`seconds` before one timed replay."""
@@ -323,7 +350,7 @@ def main():
     calls = mxnorm_calls(sets, g, 2, w.elem)
     nbytes = algorithmic_bytes(rows, hidden, w.elem)
 
-    wall, gpu_s = time_steps(calls, args.steps, args.warmup)
+    wall, gpu_s = time_steps_graph(calls, args.steps, args.warmup)
     value = nbytes * args.steps / wall / 1e9
     kern_s = gpu_s / args.steps
     achieved = nbytes / kern_s / 1e9
@@ -338,8 +365,14 @@ def main():
               "rows_per_s": round(rows * args.steps / wall, 1),
               "pct_of_peak_wall": round(100 * value / PEAK_HBM_GBS, 2),
               "buffer_sets": args.buffers,
+              "timed_region": "one replay of a HIP graph of the K captured calls",
               "clock_ramp_s_before_warmup": CLOCK_RAMP_S,
               "kernel_source_hash": kernel_hash()}
+
+    # the same K steps as direct calls through the C ABI (context)
+    dwall, dgpu = time_steps(calls, args.steps, 0)
+    extras["direct_calls_kernel_us_mean"] = round(dgpu / args.steps * 1e6, 3)
+    extras["direct_calls_wall_GBps"] = round(nbytes * args.steps / dwall / 1e9, 1)
 
     if not args.no_extras:
         head_us = graph_us(calls, 300)

@@ -234,7 +234,7 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  * computed in fp32 as dx_j = rho * (g_j - y_j * m) with y = fl(rho * x) and
  * m = (1/hidden) * sum_k y_k g_k (the same value; no intermediate overflows
  * unless dx does), and dx rounded to bf16 (nearest even); dgamma_j
- * accumulates fma(dy_j * x_j, rho, .).  dgamma is summed in an order that
+ * accumulates fma(dy_j, y_j, .).  dgamma is summed in an order that
  * depends only on (rows, hidden): results are bit-reproducible run to run.
  *   x, dy     : device bf16 [rows, hidden] (the forward's input and the
  *               gradient of its output), 16-byte aligned
@@ -247,8 +247,9 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  *               bytes, 16-byte aligned, caller-owned; required iff gamma !=
  *               NULL and rows > 0; its contents on entry do not matter
  * hidden must be a multiple of 32 and at most MXQ_MAX_HIDDEN (MXQ_EUNSUPPORTED
- * above).  The sum over a row of y.g: per-lane fused multiply-add chains over
- * the lane's 8-element chunks in order, a fixed tree over the wave, and where
+ * above).  The sum over a row of y.g: per lane, eight fused multiply-add
+ * chains (one per position in the lane's 8-element chunks, over the chunks in
+ * order) added in a fixed tree, then a fixed tree over the wave, and where
  * a row is split over 2, 4 or 8 waves (rows wider than 4096; without a gain,
  * rows wider than 2048) the wave sums added in wave order.
  * Two launches with a gain (rows, then the dgamma column sums), one without.

@@ -106,19 +106,66 @@ __device__ __forceinline__ void load_row(const BwdArgs& a, int64_t row, const ui
 // dx of one row (and its dgamma contribution added to acc).  W > 1: the row is
 // shared by the W waves of the workgroup; s_dot (2 W floats, alternating
 // halves by row parity `par`) carries their partial sums of y.g.
+// The gain staged in LDS once per workgroup: widened to fp32 (F32: half h,
+// elements 4h .. 4h+3, of 8-element chunk c at h * NCH + c, so that the lanes
+// of a wave read consecutive 16-byte slots), which takes the widening out of
+// both passes (8192 x 8192: 79.6 against 81.3 us), or as bf16 chunks for rows
+// of more than 16384 (the fp32 copy would be 128 KiB: 92.7 against 91.5 us).
+template <int NCH>
+struct GainLds {
+  static constexpr bool F32 = NCH <= 2048;
+  // 16-byte slots: two per chunk as fp32, one per chunk as bf16
+  static constexpr int kSlots = F32 ? 2 * NCH : NCH;
+};
+
+template <int NCH>
+__device__ __forceinline__ void gain8(const float4* s_gf, uint32_t c, float (&g)[8]) {
+  if constexpr (GainLds<NCH>::F32) {
+    const float4 a = s_gf[c], b = s_gf[NCH + c];
+    g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+    g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+  } else {
+    widen8(reinterpret_cast<const uint4*>(s_gf)[c], g);
+  }
+}
+
+// Stage the gain (chunks past the row end repeat the last one and are never
+// used).
+template <int NCH>
+__device__ __forceinline__ void stage_gain(const BwdArgs& a, float4* s_gf, int nthreads) {
+  const int nchunk = a.hidden >> 3;
+  for (int c = threadIdx.x; c < NCH; c += nthreads) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(a.gamma + (uint32_t)min(c, nchunk - 1) * 16u);
+    if constexpr (GainLds<NCH>::F32) {
+      float f[8];
+      widen8(raw, f);
+      s_gf[c] = make_float4(f[0], f[1], f[2], f[3]);
+      s_gf[NCH + c] = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+      reinterpret_cast<uint4*>(s_gf)[c] = raw;
+    }
+  }
+  __syncthreads();
+}
+
 template <bool GAMMA, int STEPS, int W = 1>
 __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
                                         const uint32_t (&choff)[STEPS], const bool (&act)[STEPS],
-                                        const uint4* s_gamma, uint4 (&xv)[STEPS],
+                                        const float4* s_gf, uint4 (&xv)[STEPS],
                                         uint4 (&dv)[STEPS], float (&acc)[GAMMA ? STEPS : 1][8],
                                         float* s_dot = nullptr, int wir = 0, int par = 0) {
+  constexpr int NCH = STEPS * W * kWave;  // gain chunks staged
   // rho through the constant address space: a scalar load, so waiting for it
   // never waits for vector loads issued after this row's
   const float rho = ((const __attribute__((address_space(4))) float*)a.rrms)[row];
 
-  // sum_k y_k g_k with y_k = fl(rho x_k) (fp32; per-lane FMA chain, then a
-  // fixed wave tree)
-  float dot = 0.0f;
+  // sum_k y_k g_k with y_k = fl(rho x_k), fp32: eight FMA chains per lane (one
+  // per position in the 8-element chunk, over the lane's chunks in order, so
+  // that a wave alone on its SIMD is not held by one 8 x STEPS-long dependent
+  // chain), added in a fixed tree, then a fixed tree over the wave
+  float dp[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dp[i] = 0.0f;
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     if (!act[s]) continue;
@@ -127,13 +174,14 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
     widen8(dv[s], g);
     if constexpr (GAMMA) {
       float gf[8];
-      widen8(s_gamma[choff[s] >> 4], gf);
+      gain8<NCH>(s_gf, choff[s] >> 4, gf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) g[i] = g[i] * gf[i];  // exact: 8-bit x 8-bit significands
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(xf[i] * rho, g[i], dot);
+    for (int i = 0; i < 8; ++i) dp[i] = __builtin_fmaf(xf[i] * rho, g[i], dp[i]);
   }
+  float dot = ((dp[0] + dp[1]) + (dp[2] + dp[3])) + ((dp[4] + dp[5]) + (dp[6] + dp[7]));
   dot = wave_sum_f32(dot);
   if constexpr (W > 1) {
     // The other half of s_dot is the next row's, and a wave rewrites this
@@ -162,14 +210,13 @@ __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t row, int lane,
     widen8(xv[s], xf);
     widen8(dv[s], dyf);
     float gf[8];
-    if constexpr (GAMMA) {
-      widen8(s_gamma[choff[s] >> 4], gf);
-    }
+    if constexpr (GAMMA) gain8<NCH>(s_gf, choff[s] >> 4, gf);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float g = GAMMA ? dyf[i] * gf[i] : dyf[i];
-      d[i] = rho * __builtin_fmaf(-m, xf[i] * rho, g);
-      if constexpr (GAMMA) acc[s][i] = __builtin_fmaf(dyf[i] * xf[i], rho, acc[s][i]);
+      const float y = xf[i] * rho;
+      d[i] = rho * __builtin_fmaf(-m, y, g);
+      if constexpr (GAMMA) acc[s][i] = __builtin_fmaf(dyf[i], y, acc[s][i]);
     }
     store_nt16(drow + choff[s], bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]),
                bf16x2_rne(d[4], d[5]), bf16x2_rne(d[6], d[7]));
@@ -192,13 +239,9 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
     choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;
   }
 
-  // the gain is read once per workgroup into LDS (the kernel is persistent)
-  __shared__ uint4 s_gamma[GAMMA ? STEPS * kWave : 1];
-  if constexpr (GAMMA) {
-    for (int c = threadIdx.x; c < STEPS * kWave; c += NW * kWave)
-      s_gamma[c] = *reinterpret_cast<const uint4*>(a.gamma + (uint32_t)min(c, nchunk - 1) * 16u);
-    __syncthreads();
-  }
+  // the gain is widened once per workgroup into LDS (the kernel is persistent)
+  __shared__ float4 s_gf[GAMMA ? GainLds<STEPS * kWave>::kSlots : 1];
+  if constexpr (GAMMA) stage_gain<STEPS * kWave>(a, s_gf, NW * kWave);
 
   float acc[GAMMA ? STEPS : 1][8];
 #pragma unroll
@@ -220,19 +263,19 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
     while (row < a.rows) {
       const int64_t r1 = row + stride;
       load_row<STEPS>(a, r1 < a.rows ? r1 : row, choff, xb, db);
-      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xa, da, acc);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gf, xa, da, acc);
       row = r1;
       if (row >= a.rows) break;
       const int64_t r2 = row + stride;
       load_row<STEPS>(a, r2 < a.rows ? r2 : row, choff, xa, da);
-      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xb, db, acc);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gf, xb, db, acc);
       row = r2;
     }
   } else {
     if (row < a.rows) {  // one row per wave, as in the forward
       uint4 xv[STEPS], dv[STEPS];
       load_row<STEPS>(a, row, choff, xv, dv);
-      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gamma, xv, dv, acc);
+      bwd_row<GAMMA, STEPS>(a, row, lane, choff, act, s_gf, xv, dv, acc);
     }
   }
 
@@ -279,12 +322,8 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
     choff[s] = (uint32_t)(FULL ? ch : min(ch, nchunk - 1)) * 16u;
   }
   __shared__ float s_dot[2 * W];
-  __shared__ uint4 s_gamma[GAMMA ? STEPS * W * kWave : 1];
-  if constexpr (GAMMA) {
-    for (int c = threadIdx.x; c < STEPS * W * kWave; c += W * kWave)
-      s_gamma[c] = *reinterpret_cast<const uint4*>(a.gamma + (uint32_t)min(c, nchunk - 1) * 16u);
-    __syncthreads();
-  }
+  __shared__ float4 s_gf[GAMMA ? GainLds<STEPS * W * kWave>::kSlots : 1];
+  if constexpr (GAMMA) stage_gain<STEPS * W * kWave>(a, s_gf, W * kWave);
   float acc[GAMMA ? STEPS : 1][8];
 #pragma unroll
   for (int s = 0; s < (GAMMA ? STEPS : 1); ++s)
@@ -300,7 +339,7 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
     for (; row < a.rows; row += stride) {
       uint4 xv[STEPS], dv[STEPS];
       load_row<STEPS>(a, row, choff, xv, dv);
-      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xv, dv, acc, s_dot, wir, par);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gf, xv, dv, acc, s_dot, wir, par);
       par ^= 1;
     }
   } else if constexpr (GAMMA) {
@@ -311,13 +350,13 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
     while (row < a.rows) {
       const int64_t r1 = row + stride;
       load_row<STEPS>(a, r1 < a.rows ? r1 : row, choff, xb, db);
-      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xa, da, acc, s_dot, wir, par);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gf, xa, da, acc, s_dot, wir, par);
       par ^= 1;
       row = r1;
       if (row >= a.rows) break;
       const int64_t r2 = row + stride;
       load_row<STEPS>(a, r2 < a.rows ? r2 : row, choff, xa, da);
-      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xb, db, acc, s_dot, wir, par);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gf, xb, db, acc, s_dot, wir, par);
       par ^= 1;
       row = r2;
     }
@@ -336,7 +375,7 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
     if (row < a.rows) {
       uint4 xv[STEPS], dv[STEPS];
       load_row<STEPS>(a, row, choff, xv, dv);
-      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gamma, xv, dv, acc, s_dot, wir, 0);
+      bwd_row<GAMMA, STEPS, W>(a, row, lane, choff, act, s_gf, xv, dv, acc, s_dot, wir, 0);
     }
   }
 }
