@@ -171,15 +171,13 @@ __device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, fl
 // ([P1] §2 "Implementacion": scale the values and produce the quantisation
 // scales in the same pass; [P3]: H16 / H32 rotation before the MXFP4 cast.)
 template <int ELEM, bool GAMMA, int HAD>
-__device__ __forceinline__ uint32_t cast_chunk(const float (&x)[8], const uint4 gv, float rho,
+__device__ __forceinline__ uint32_t cast_chunk(const float (&x)[8], const float (&g)[8], float rho,
                                                int lane, uint8_t* __restrict__ dst) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = x[i] * rho;
   if constexpr (GAMMA) {
-    float g[8];
-    widen8(gv, g);
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] * g[i];
   }
@@ -244,10 +242,23 @@ struct RowRegs {
 
 // The whole forward of one row held in VGPRs (v: the row; s_gain: the gain,
 // staged in LDS, chunk s * 64 + lane at index s * 64 + lane).
+// How k_mxnorm_wave stages the gain in LDS: rows of 4 or 8 chunks per lane
+// widen it to fp32 once per workgroup (half h, elements 4h .. 4h+3, of chunk c
+// at h * NCH + c, so that the lanes of a wave read consecutive 16-byte slots),
+// which takes 8 widening instructions per chunk out of the cast (8192 x 2048:
+// 10.20 against 10.35 us); shorter rows keep the bf16 copy by LDS-DMA, whose
+// shorter path to LDS is what the small, latency-bound launches need (256 x
+// 768: 2.15 against 2.26 us).
+template <int STEPS>
+struct WaveGain {
+  static constexpr bool F32 = STEPS >= 4;
+  static constexpr int kSlots = F32 ? 2 * STEPS * kWave : STEPS * kWave;  // 16-byte slots
+};
+
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lane,
                                          const bool (&act)[STEPS], const uint4 (&v)[STEPS],
-                                         const uint4* s_gain, uint32_t* __restrict__ s_sc) {
+                                         const float4* s_gain, uint32_t* __restrict__ s_sc) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   const int K = a.hidden >> 5;
@@ -279,11 +290,17 @@ __device__ __forceinline__ void wave_row(const WaveArgs& a, int64_t row, int lan
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     if (!FULL && !act[s]) continue;  // quad-uniform; the DPP inside stays in the quad
-    const uint4 gv = GAMMA ? s_gain[s * kWave + lane] : make_uint4(0, 0, 0, 0);
-    float x[8];
+    float x[8], gf[8];
     rr.values(v, s, x);
+    if constexpr (GAMMA && WaveGain<STEPS>::F32) {
+      const float4 g0 = s_gain[s * kWave + lane], g1 = s_gain[STEPS * kWave + s * kWave + lane];
+      gf[0] = g0.x; gf[1] = g0.y; gf[2] = g0.z; gf[3] = g0.w;
+      gf[4] = g1.x; gf[5] = g1.y; gf[6] = g1.z; gf[7] = g1.w;
+    } else if constexpr (GAMMA) {
+      widen8(reinterpret_cast<const uint4*>(s_gain)[s * kWave + lane], gf);
+    }
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(
-        x, gv, rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
+        x, gf, rho, lane, crow + (uint32_t)(s * kWave + lane) * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc)[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
   // the scale bytes written above are read back by other lanes of the wave
@@ -321,19 +338,32 @@ __device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[ST
 // 34.0 against 34.6 us; H16 -> E2M1 at 32768 x 4096: 60.9 against 62.6 us.
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
 __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+  constexpr int NCH = STEPS * kWave;  // chunk slots of a row
+  constexpr bool GF32 = WaveGain<STEPS>::F32;
   __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
-  __shared__ uint4 s_gain[GAMMA ? STEPS * kWave : 1];
+  __shared__ float4 s_gain[GAMMA ? WaveGain<STEPS>::kSlots : 1];  // layout: WaveGain
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  const bool row_ok = row < a.rows;  // waves past the end still copy the gain and meet the barrier
+  const bool row_ok = row < a.rows;  // waves past the end still stage the gain and meet the barrier
 
   uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
   bool act[STEPS];
   lane_chunks<STEPS, FULL>(lane, a.hidden >> 3, act, choff);
-  if constexpr (GAMMA) {
-    // wave w copies steps w, w + 4 of the gain; chunks past the row end read
-    // as zero (buffer range) and are never used
+  constexpr int kGainPerThread = (NCH + kThreads - 1) / kThreads;
+  uint4 graw[GAMMA && GF32 ? kGainPerThread : 1];
+  if constexpr (GAMMA && GF32) {
+    // thread i loads chunks i, i + 256 of the gain (chunks past the row end
+    // repeat the last one and are never used)
+    const int last = (a.hidden >> 3) - 1;
+#pragma unroll
+    for (int j = 0; j < kGainPerThread; ++j) {
+      const int c = j * kThreads + (int)threadIdx.x;
+      graw[j] = reinterpret_cast<const uint4*>(a.gamma)[min(c, last)];
+    }
+  } else if constexpr (GAMMA) {
+    // wave w copies steps w, w + 4 of the gain by LDS-DMA; chunks past the
+    // row end read as zero (buffer range) and are never used
     const rsrc_t rg = row_rsrc(a.gamma, (uint32_t)a.hidden * 2u);
 #pragma unroll
     for (int j = 0; j < (STEPS + 3) / 4; ++j) {
@@ -344,14 +374,26 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
             (int)((uint32_t)(s * kWave + lane) * 16u), 0, 0, 0);
     }
   }
-  // The wait below counts on the gain copies being issued before the row
-  // loads; this compiler barrier keeps any row load from being moved above them.
+  // The gain loads stay ahead of the row loads (the LDS-DMA wait below counts
+  // on that order).
   if constexpr (GAMMA) asm volatile("" ::: "memory");
   const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
   uint4 v[STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) v[s] = load_stream16(xrow + choff[s]);
-  if constexpr (GAMMA) {
+  if constexpr (GAMMA && GF32) {
+#pragma unroll
+    for (int j = 0; j < kGainPerThread; ++j) {
+      const int c = j * kThreads + (int)threadIdx.x;
+      if (c < NCH) {
+        float f[8];
+        widen8(graw[j], f);
+        s_gain[c] = make_float4(f[0], f[1], f[2], f[3]);
+        s_gain[NCH + c] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+    __syncthreads();
+  } else if constexpr (GAMMA) {
     // the copies were issued before the STEPS row loads: at most STEPS loads
     // outstanding means the copies have landed
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(STEPS) : "memory");
@@ -798,10 +840,10 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
   for (int s = 0; s < STEPS; ++s) {
     if (!act[s]) continue;  // quad-uniform
     const int ch = (wir * STEPS + s) * kWave + lane;
-    const uint4 gv = GAMMA ? s_gain[ch] : make_uint4(0, 0, 0, 0);
-    float x[8];
+    float x[8], gf[8];
     rr.values(v, s, x);
-    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(x, gv, rho, lane,
+    if constexpr (GAMMA) widen8(s_gain[ch], gf);
+    const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(x, gf, rho, lane,
                                                      crow + (uint32_t)ch * (uint32_t)CB);
     reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
