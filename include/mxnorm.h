@@ -57,24 +57,35 @@ typedef enum {
     MXQ_EINVAL = -1,        /* bad shape, NULL pointer, bad p / c / eps / had */
     MXQ_EALIGN = -2,        /* a pointer is not aligned as required above */
     MXQ_EUNSUPPORTED = -3,  /* valid arguments outside what the library supports */
-    MXQ_EHIP = -4           /* the HIP runtime refused the launch */
+    MXQ_EHIP = -4,          /* the HIP runtime refused the launch */
+    MXQ_STATUS_MIN_ = -2147483647 - 1,  /* not statuses: the type spans int */
+    MXQ_STATUS_MAX_ = 2147483647
 } mxq_status;
 
+/* The argument enums below span the whole int range (the _MIN_ / _MAX_
+ * enumerators are not values of the type): a caller may pass any int, and the
+ * library rejects values outside the listed ones with MXQ_EINVAL. */
 typedef enum {
     MXQ_E4M3 = 0,           /* MXFP8: E4M3 elements, 1 byte each */
-    MXQ_E2M1 = 1            /* MXFP4: E2M1 elements, 2 per byte */
+    MXQ_E2M1 = 1,           /* MXFP4: E2M1 elements, 2 per byte */
+    MXQ_ELEM_MIN_ = -2147483647 - 1,
+    MXQ_ELEM_MAX_ = 2147483647
 } mxq_elem;
 
 /* Which block magnitude enters the MXNorm power mean. */
 typedef enum {
     MXQ_SRC_SCALES = 0,     /* 2^(e_k + emax): the E8M0 scale of block k as a power of two */
-    MXQ_SRC_ABSMAX = 1      /* the exact block absmax max_i |x_i| */
+    MXQ_SRC_ABSMAX = 1,     /* the exact block absmax max_i |x_i| */
+    MXQ_SRC_MIN_ = -2147483647 - 1,
+    MXQ_SRC_MAX_ = 2147483647
 } mxq_source;
 
 /* Element type of a matrix-product output. */
 typedef enum {
     MXQ_OUT_F32 = 0,        /* fp32 */
-    MXQ_OUT_BF16 = 1        /* bf16: the fp32 result rounded to nearest even */
+    MXQ_OUT_BF16 = 1,       /* bf16: the fp32 result rounded to nearest even */
+    MXQ_OUT_MIN_ = -2147483647 - 1,
+    MXQ_OUT_MAX_ = 2147483647
 } mxq_out;
 
 #define MXQ_BLOCK 32

@@ -31,7 +31,8 @@ OUT_BF16 = 1
 MAX_HIDDEN = 32768
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "lib", "libmxnorm.so")
+# MXQ_LIB overrides the path (e.g. a host-sanitizer build of the same sources)
+_LIB_PATH = os.environ.get("MXQ_LIB") or os.path.join(_HERE, "lib", "libmxnorm.so")
 _lib = None
 
 EXPORTED = ("mx_quant", "mxnorm_fwd", "mxnorm_hadamard_fwd", "rmsnorm_mxquant_fwd",

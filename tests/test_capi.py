@@ -68,8 +68,18 @@ def test_fwd_ex_argument_checks():
 
 
 def test_status_strings():
-    for s in (OK, EINVAL, EALIGN, EUNSUP, -4):
+    for s in (OK, EINVAL, EALIGN, EUNSUP, -4, -5, 7, -2 ** 31, 2 ** 31 - 1):
         assert mxq.status_str(s).startswith("MXQ_")
+    assert mxq.status_str(-5) == "MXQ_UNKNOWN"
+
+
+def test_enum_arguments_outside_their_values_are_rejected():
+    # any int is a valid argument value (the enums span int); the checks reject it
+    L = mxq.lib()
+    for bad in (2, -1, 2 ** 31 - 1, -2 ** 31):
+        assert L.mx_quant(A16, 4, 64, bad, A16, A16, None) == EINVAL
+        assert L.mxnorm_default_c_for(2, bad) == 0.0
+        assert L.mx_matmul(A16, A16, A16, A16, 128, 128, 256, A16, bad, None) == EINVAL
 
 
 def _mxq(x=A16, rows=4, hidden=64, elem=0, codes=A16, scales=A16):
