@@ -55,8 +55,8 @@ namespace {
 
 constexpr int kBwdThreads = 256;  // 4 waves per workgroup without a gain
 constexpr int kColsumThreads = 256;
-constexpr int kColsumCols = 16;    // columns per workgroup of the partial-row sum
-constexpr int kColsumSlices = 64;  // partial rows b = slice + 64 k per thread
+constexpr int kColsumCols = 32;    // columns per workgroup of the partial-row sum (128 B of a row)
+constexpr int kColsumSlices = 32;  // partial rows b = slice + 32 k per thread
 constexpr int kColsumLoads = (int)((kBwdMaxPartials + kColsumSlices - 1) / kColsumSlices);
 
 constexpr int kBwdWaves = 4;  // waves per workgroup of the persistent (gain) kernel
@@ -382,17 +382,19 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
 
 // dgamma_j = sum over the G <= kBwdMaxPartials partial rows, in a fixed order.
 // Thread (slice, q) of a workgroup loads the float4 of columns 4q..4q+3 of
-// partial rows slice, slice + 64, ... (all loads issued before the adds) and
-// adds them in that order; the 64 slice sums of a column are then added in
-// four runs of 16 consecutive slices, and the four run sums in order.
+// partial rows slice, slice + 32, ... (all loads issued before the adds; a
+// load instruction reads full 128-byte lines of 8 partial rows) and adds them
+// in that order; the 32 slice sums of a column are then added in four runs of
+// 8 consecutive slices, and the four run sums in order.  (16 columns per
+// workgroup read half lines: 2048 x 32768, 256 partial rows: 11.6 us.)
 __global__ __launch_bounds__(kColsumThreads) void k_colsum(const float* __restrict__ partial,
                                                            int G, int hidden,
                                                            float* __restrict__ out) {
   __shared__ float s_part[kColsumSlices][kColsumCols];
   __shared__ float s_run[4][kColsumCols];
-  const int q = threadIdx.x & 3;
-  const int slice = threadIdx.x >> 2;
-  const int col0 = blockIdx.x * kColsumCols + q * 4;  // hidden % 16 == 0: in range
+  const int q = threadIdx.x & 7;
+  const int slice = threadIdx.x >> 3;
+  const int col0 = blockIdx.x * kColsumCols + q * 4;  // hidden % 32 == 0: in range
   float4 v[kColsumLoads];
 #pragma unroll
   for (int k = 0; k < kColsumLoads; ++k) {
@@ -412,9 +414,10 @@ __global__ __launch_bounds__(kColsumThreads) void k_colsum(const float* __restri
   __syncthreads();
   if (threadIdx.x < 4 * kColsumCols) {
     const int c = threadIdx.x % kColsumCols, run = threadIdx.x / kColsumCols;
-    float t = s_part[run * 16][c];
+    constexpr int kRun = kColsumSlices / 4;
+    float t = s_part[run * kRun][c];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) t += s_part[run * 16 + i][c];
+    for (int i = 1; i < kRun; ++i) t += s_part[run * kRun + i][c];
     s_run[run][c] = t;
   }
   __syncthreads();
