@@ -7,8 +7,9 @@
 //   [P3] MXFP4 pre-training on AMD MI355X (gist.science summary),
 //        "Metodologia", "Hallazgos" 2 (deterministic H16 / H32 rotation).
 //
-// Every kernel here is an HBM-bandwidth-bound streaming codec: there is no
-// dense contraction on this path, so no MFMA.  The design points are
+// Every kernel here is a streaming codec bound by HBM bandwidth (the rotation
+// kernels with their VALU work close behind): there is no dense contraction on
+// this path, so no MFMA.  The design points are
 //   * a lane owns 8 consecutive bf16 (one 16-byte load); a quad of lanes owns
 //     a 32-element MX block, so block reductions are two quad DPP steps;
 //   * one wavefront owns a whole row (hidden <= 2048, and rotated rows up to
@@ -20,10 +21,11 @@
 //     measured faster than one (16384 x 4096: 33.4 against 34.0 us; E2M1 27.7
 //     against 28.9 us): a wave's cast is half as long, and the cast of the
 //     rows that arrive last is what the launch waits for at its end (with H16
-//     one wave per row stays faster);
+//     one wave per row stays faster); for the same reason the last 2048 rows
+//     of an E4M3 launch of 8192 rows or more are cast by 4 waves each;
 //   * x is loaded and the codes stored non-temporally (each byte is touched
-//     once); the gain comes from L2, staged once per workgroup in LDS by
-//     LDS-DMA loads;
+//     once); the gain comes from L2, staged once per workgroup in LDS (by
+//     LDS-DMA loads as bf16, or widened to fp32 where that measured faster);
 //   * workgroups keep the hardware's round-robin spread over the 8 XCDs, so
 //     the whole chip sweeps one contiguous region of HBM at a time (giving
 //     each XCD its own contiguous range of rows measured ~5% slower).
@@ -211,6 +213,8 @@ struct WaveArgs {
   uint8_t* scales;
   float* rrms;
   int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
+  int64_t head_blocks;  // k_mxnorm_wide: workgroups before the tail part
+  int64_t tail_rows;    // k_mxnorm_wide: rows of the tail part (at the end)
 };
 
 // Rows of up to 4 chunks per lane are widened to fp32 once, before the row
@@ -755,27 +759,31 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_lane32(const WaveArgs a) {
 // (wir*STEPS + s)*64 + lane at step s: each wave streams its own contiguous
 // part of the row (measured 0.6-1.4% faster at 8192 and 32768 than waves
 // interleaving 1 KiB steps, the same at 4096).
+//
+// The rows of workgroup `blk` of this part are row0 + blk * RPW + rslot, those
+// below `rlim` valid.  LDS: s_max, s_sum [NW], s_sc [NW * STEPS * 4] (each
+// wave's scale bytes, 16 per step), s_gain [W * STEPS * 64] (the row's gain,
+// chunk c at c).
 // ----------------------------------------------------------------------------------
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
-__global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const WaveArgs a) {
+__device__ __forceinline__ void wide_rows(const WaveArgs& a, int64_t blk, int64_t row0,
+                                          int64_t rlim, int* s_max, double* s_sum,
+                                          uint32_t* s_sc, uint4* s_gain) {
   constexpr int EMAX = Elem<ELEM>::kEmax;
   constexpr int CB = Elem<ELEM>::kCodeBytesPerLane;
   constexpr int NW = W > 4 ? W : 4;  // waves per workgroup
   constexpr int RPW = NW / W;        // rows per workgroup
   static_assert(W == 2 || W == 4 || W == 8, "waves per row");
-  __shared__ int s_max[NW];
-  __shared__ double s_sum[NW];
-  __shared__ uint32_t s_sc[NW][STEPS * 4];  // each wave's scale bytes, 16 per step
-  __shared__ uint4 s_gain[GAMMA ? W * STEPS * kWave : 1];  // the row's gain, chunk c at c
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rslot = wave / W;
   const int wir = wave % W;
-  const int64_t row = (int64_t)blockIdx.x * RPW + rslot;
-  const bool row_ok = row < a.rows;  // waves past the end still join the barriers
+  const int64_t row = row0 + blk * RPW + rslot;
+  const bool row_ok = row < rlim;  // waves past the end still join the barriers
   const int nchunk = a.hidden >> 3;
   const int K = a.hidden >> 5;
+  uint32_t* const wsc = s_sc + wave * STEPS * 4;
 
   // The gain is staged in LDS by LDS-DMA loads issued ahead of the row loads
   // (wave w copies chunk groups w, w + NW, ...; chunks past the row end read
@@ -845,7 +853,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     if constexpr (GAMMA) widen8(s_gain[ch], gf);
     const uint32_t sb = cast_chunk<ELEM, GAMMA, HAD>(x, gf, rho, lane,
                                                      crow + (uint32_t)ch * (uint32_t)CB);
-    reinterpret_cast<uint8_t*>(s_sc[wave])[s * 16 + (lane >> 2)] = (uint8_t)sb;
+    reinterpret_cast<uint8_t*>(wsc)[s * 16 + (lane >> 2)] = (uint8_t)sb;
   }
   // Step s of this wave covers blocks (wir STEPS + s) * 16 .. + 15 of the row: 16
   // scale bytes gathered in LDS, written as four dwords (or bytes when the
@@ -857,7 +865,7 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
     const int s = lane >> 2, q = lane & 3;  // step, dword within the step
     if (s < STEPS && row_ok) {
       const int b0 = (wir * STEPS + s) * 16;  // first block of the step
-      if (b0 + 4 * q < K) reinterpret_cast<uint32_t*>(srow + b0)[q] = s_sc[wave][s * 4 + q];
+      if (b0 + 4 * q < K) reinterpret_cast<uint32_t*>(srow + b0)[q] = wsc[s * 4 + q];
     }
   } else {
 #pragma unroll
@@ -866,9 +874,40 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
       const int s = i >> 4;
       const int blk = (wir * STEPS + s) * 16 + (i & 15);
       if (s < STEPS && row_ok && blk < K)
-        srow[blk] = reinterpret_cast<const uint8_t*>(s_sc[wave])[i];
+        srow[blk] = reinterpret_cast<const uint8_t*>(wsc)[i];
     }
   }
+}
+
+
+// Rows per launch that k_mxnorm_wide<2 waves, 4 steps> hands, at the end of
+// the grid, to workgroups owning one row with 4 waves (E4M3 only).  The launch
+// ends on the row statistic and cast of the rows whose data arrive last; in
+// the last dispatch round (2048 rows = 8192 waves) each wave then casts half
+// as much.  Measured at hidden 4096, E4M3 with gain: 8192 rows 17.91 against
+// 18.52 us, 16384 rows 32.99 against 33.54 us, 32768 rows 63.73 against 64.37
+// us, 65536 rows within noise; E2M1 (a shorter cast per element) was slower.
+constexpr int64_t kWideTailRows = 2048;
+constexpr int64_t kWideTailMinRows = 8192;
+
+template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
+__global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const WaveArgs a) {
+  constexpr int NW = W > 4 ? W : 4;
+  __shared__ int s_max[NW];
+  __shared__ double s_sum[NW];
+  __shared__ uint32_t s_sc[NW * STEPS * 4];
+  __shared__ uint4 s_gain[GAMMA ? W * STEPS * kWave : 1];
+  if constexpr (ELEM == 0 && W == 2 && STEPS == 4) {
+    // the tail part: same LDS footprint (4 waves x 2 steps of the same row width)
+    if ((int64_t)blockIdx.x >= a.head_blocks) {
+      wide_rows<ELEM, GAMMA, HAD, 4, 2, SRC>(a, (int64_t)blockIdx.x - a.head_blocks,
+                                            a.rows - a.tail_rows, a.rows, s_max, s_sum, s_sc,
+                                            s_gain);
+      return;
+    }
+  }
+  wide_rows<ELEM, GAMMA, HAD, W, STEPS, SRC>(a, blockIdx.x, 0, a.rows - a.tail_rows, s_max,
+                                            s_sum, s_sc, s_gain);
 }
 
 // ----------------------------------------------------------------------------------
@@ -1037,6 +1076,8 @@ WaveArgs wave_args(const MxnormArgs& m) {
   a.scales = m.scales;
   a.rrms = m.rrms;
   a.scales_dwords = ((m.hidden / 32) % 4 == 0) && (((uintptr_t)m.scales & 3) == 0);
+  a.head_blocks = 0;
+  a.tail_rows = 0;
   return a;
 }
 
@@ -1055,9 +1096,11 @@ hipError_t launch_wave(const MxnormArgs& m) {
 
 template <int ELEM, bool GAMMA, int HAD, int SRC, int W, int STEPS>
 hipError_t launch_wide(const MxnormArgs& m) {
-  const WaveArgs a = wave_args(m);
+  WaveArgs a = wave_args(m);
   constexpr int NW = W > 4 ? W : 4, RPW = NW / W;
-  const dim3 grid((unsigned)((m.rows + RPW - 1) / RPW));
+  a.tail_rows = (ELEM == 0 && W == 2 && STEPS == 4 && m.rows >= kWideTailMinRows) ? kWideTailRows : 0;
+  a.head_blocks = (m.rows - a.tail_rows + RPW - 1) / RPW;
+  const dim3 grid((unsigned)(a.head_blocks + a.tail_rows));
   hipLaunchKernelGGL((k_mxnorm_wide<ELEM, GAMMA, HAD, W, STEPS, SRC>), grid, dim3(NW * kWave),
                      0, (hipStream_t)m.stream, a);
   return hipGetLastError();
@@ -1089,8 +1132,9 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
   if (r.waves == 1 && r.steps == 8) {
     // 2048 < hidden <= 4096: 2 waves per row, except with a rotation (its
-    // longer cast per element runs faster one wave per row); H32, and H16
-    // with a gain, on rows of exactly 4096 with whole 16-groups per lane
+    // longer cast per element runs faster one wave per row); on rows of
+    // exactly 4096, E2M1 rotations with a whole 32-group per lane, H32 and
+    // H16 with a gain to E4M3 with whole 16-groups per lane
     if constexpr (HAD == 0) {
       return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
     } else {

@@ -180,6 +180,47 @@ def test_mxnorm_edge_rows(elem, p, hidden):
         _check_mxnorm(xb, None, p, c, elem, what="edge no gamma c=%g" % c)
 
 
+@pytest.mark.parametrize("rows", [8191, 8192, 8193, 10001])
+@pytest.mark.parametrize("hidden", [3072, 4064, 4096])
+def test_mxnorm_wide_tail_part(rows, hidden):
+    """E4M3 launches of 8192 rows or more over 2048 < hidden <= 4096 hand
+    their last 2048 rows to workgroups of one row and 4 waves: the boundary
+    between the two parts (odd row counts leave the last 2-row workgroup half
+    empty), ragged widths, and edge rows placed in the tail part."""
+    xb, gb = W.generate(rows, hidden, "rowscale", seed=rows + hidden)
+    e = _edge_rows(hidden)
+    xb[rows - 1 - len(e):rows - 1] = e          # in the tail part
+    xb[rows - 2048 - 3:rows - 2048 + 3] = e[:6]  # across the boundary
+    for p, c in ((2, C_DEF[2]), (1, 0.3)):
+        _check_mxnorm(xb, gb, p, c, 0, what="tail rows=%d D=%d p=%d" % (rows, hidden, p))
+    _check_mxnorm(xb, None, 2, 10.0, 0, what="tail rows=%d D=%d no gamma" % (rows, hidden))
+
+
+def test_mxnorm_wide_tail_part_sampled():
+    # a large E4M3 launch at hidden 4096 (the head part 292 K workgroups, then
+    # 2048 one-row workgroups), checked on sampled rows the oracle computes one
+    # by one, every row around the boundary of the two parts included
+    rows, hidden = 600001, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(37)
+    x = (torch.randn(rows, hidden, device="cuda", generator=gen) * 2.0).to(torch.bfloat16)
+    g = (1 + 0.02 * torch.randn(hidden, device="cuda", generator=gen)).to(torch.bfloat16)
+    print("case: mxnorm_fwd rows=%d hidden=%d" % (rows, hidden), flush=True)
+    codes, scales, rho = mxq.mxnorm_fwd(x, g, p=2, c=C_DEF[2], elem=O.E4M3)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(37)
+    b = rows - 2048
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 1500), np.arange(b - 4, b + 4),
+                                    [0, 1, rows - 2, rows - 1]]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = x[ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    gs = g.view(torch.int16).cpu().numpy().view(np.uint16)
+    oc, os_, orr = O.mxnorm_fwd(xs, gs, 2, C_DEF[2], O.E4M3)
+    P.assert_rho_equal(rho[ti].cpu().numpy(), orr, "tail sampled")
+    P.assert_scales_equal(scales[ti].cpu().numpy(), os_, "tail sampled")
+    P.assert_codes(codes[ti].cpu().numpy(), oc, os_, O.E4M3, exact=True, what="tail sampled")
+
+
 def test_mxnorm_default_c_and_optional_rrms():
     xb, gb = W.generate(64, 4096, "outlier", seed=5)
     x, g = P.to_device_bf16(xb), P.to_device_bf16(gb)
