@@ -40,11 +40,10 @@ hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, 
 
 // Straight-through MXNorm backward.  hidden <= kBwdMaxHidden.
 constexpr int kBwdMaxHidden = 32768;
-// Persistent workgroups of the backward with a gain (192 of 4 waves at hidden
-// <= 4096; 512 of 2 waves, 256 of 4 or 8 waves for wider rows); tuned on
-// MI355X, where fewer rows in flight stream faster for this kernel.
-constexpr int64_t kBwdMaxGroups = 192;
-constexpr int64_t kBwdMaxPartials = 512;  // most partial dgamma rows (W = 2)
+// Persistent workgroups of the backward with a gain, at most (one dgamma
+// partial row each): 512, 256 or 216 of 4 waves for rows of up to 1024, 2048
+// or 4096 elements; 512 of 2 waves, 256 of 4 or 8 waves for wider rows.
+constexpr int64_t kBwdMaxPartials = 512;
 
 struct BwdLaunch {
   const void* x;

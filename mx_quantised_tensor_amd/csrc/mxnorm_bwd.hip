@@ -21,10 +21,12 @@
 //   * with a gain, waves are persistent over rows (row += total waves) so that
 //     each lane accumulates its columns' dgamma in registers across many
 //     rows, and each wave keeps the next row's loads in flight while it works
-//     on the current one.  Only 192 workgroups of 4 waves run (768 waves,
-//     ~1500 rows in flight): measured on MI355X, more concurrent waves make
-//     this pattern slower (8 waves per CU: +18%; 3 waves per SIMD: +14%),
-//     and 128 workgroups are too few.  At the end the 4 waves of a workgroup
+//     on the current one.  At rows of 4096 only 216 workgroups of 4 waves
+//     run (864 waves, ~1700 rows in flight): measured on MI355X, more
+//     concurrent waves make this pattern slower (8 waves per CU: +18%; 3
+//     waves per SIMD: +14%), and 128 workgroups are too few; narrower rows,
+//     with fewer bytes in flight per wave, take up to 512 workgroups (see
+//     bwd_groups).  At the end the 4 waves of a workgroup
 //     add their accumulators through LDS in a fixed order and the workgroup
 //     writes one partial row; a second kernel adds the partial rows column
 //     by column in a fixed order.  Both orders depend only on (rows, hidden),
@@ -507,8 +509,18 @@ int bwd_waves_per_row(int hidden) {
 int64_t bwd_groups(int64_t rows, int hidden) {
   const int w = bwd_waves_per_row(hidden);
   if (w == 1) {
+    // measured on MI355X with 4 waves per workgroup (the partial-row sum
+    // included): rows of 512 or 1024 elements (1 or 2 chunks per lane, fewer
+    // bytes in flight per wave) stream fastest with 512 workgroups (131072 x
+    // 512: 68.5 against 101.5 us with 192; 65536 x 1024: 70.9 against 82.2),
+    // rows of 2048 with 256 (16384 x 2048: 37.2 against 38.4), rows of 3072
+    // and 4096 with 216 (16384 x 4096: 71.8-72.0 against 72.6-73.2; 16384 x
+    // 3072: 57.9-58.2 against 60.4-60.9), where more concurrent rows stream
+    // slower (256: +3%)
+    const int nchunk = hidden / 8;
+    const int64_t cap = nchunk <= 128 ? 512 : nchunk <= 256 ? 256 : 216;
     const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
-    return need < kBwdMaxGroups ? need : kBwdMaxGroups;
+    return need < cap ? need : cap;
   }
   // measured on MI355X at 16384 x 4096 / W rows (the partial-row sum included):
   // 512 workgroups for W = 2, 256 for W = 4 and W = 8

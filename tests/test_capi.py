@@ -150,7 +150,14 @@ def test_bwd_workspace_size():
     assert ws(0, 4096) == 0
     assert ws(1, 64) == 64 * 4            # one workgroup
     assert ws(5, 64) == 2 * 64 * 4        # ceil(5 / 4) workgroups of 4 waves
-    assert ws(16384, 4096) == 192 * 4096 * 4
+    # one wave per row: 512, 256 and 216 workgroups at most for rows of up to
+    # 1024, 2048 and 4096 elements
+    assert ws(16384, 4096) == 216 * 4096 * 4
+    assert ws(16384, 3072) == 216 * 3072 * 4
+    assert ws(16384, 2048) == 256 * 2048 * 4
+    assert ws(16384, 1024) == 512 * 1024 * 4
+    assert ws(16384, 512) == 512 * 512 * 4
+    assert ws(1000, 512) == 250 * 512 * 4
     # wider rows: one row at a time per workgroup of W waves, 512 workgroups
     # at most for W = 2 and 256 for W = 4, 8
     assert ws(16, 8192) == 16 * 8192 * 4
