@@ -93,15 +93,39 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// LDS reads with a constant byte offset in the instruction's offset field (the
+// fragments of a wave's four 32-row blocks are 4 KiB apart, their scale
+// records 512 bytes apart: one address register serves all four).
+template <int OFF>
 __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   v4i v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
 }
+template <int OFF>
 __device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   uint32_t v;
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
+}
+// Block blk (0..3, a constant once the callers' loops are unrolled).
+__device__ __forceinline__ v4i lds_read16_blk(uint32_t addr, int blk) {
+  switch (blk) {
+    case 0: return lds_read16<0>(addr);
+    case 1: return lds_read16<32 * kCopyK>(addr);
+    case 2: return lds_read16<64 * kCopyK>(addr);
+    default: return lds_read16<96 * kCopyK>(addr);
+  }
+}
+__device__ __forceinline__ uint32_t lds_read4_blk(uint32_t addr, int blk) {
+  switch (blk) {
+    case 0: return lds_read4<0>(addr);
+    case 1: return lds_read4<32 * kScaleRec>(addr);
+    case 2: return lds_read4<64 * kScaleRec>(addr);
+    default: return lds_read4<96 * kScaleRec>(addr);
+  }
 }
 
 template <int N>
@@ -151,14 +175,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
   // swizzle is that of fr and its scale-record rotation is (fr >> 3) & 3.
   const int fz = (fr & 7) ^ ((fr >> 3) & 3);
   const int srot = (fr >> 3) & 3;
-  uint32_t a_off[4], b_off[4], as_off[4], bs_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kCopyK);
-    b_off[i] = kSlice + (uint32_t)((wn * 128 + i * 32 + fr) * kCopyK);
-    as_off[i] = (uint32_t)((wm * 128 + i * 32 + fr) * kScaleRec);
-    bs_off[i] = kTile * kScaleRec + (uint32_t)((wn * 128 + i * 32 + fr) * kScaleRec);
-  }
+  // block i of the wave's fragments at + i * 32 rows (immediate offsets)
+  const uint32_t a_off = (uint32_t)((wm * 128 + fr) * kCopyK);
+  const uint32_t b_off = kSlice + (uint32_t)((wn * 128 + fr) * kCopyK);
+  const uint32_t as_off = (uint32_t)((wm * 128 + fr) * kScaleRec);
+  const uint32_t bs_off = kTile * kScaleRec + (uint32_t)((wn * 128 + fr) * kScaleRec);
   // chunk offset of sub-stage half v (of a copy stage), k-block h
   uint32_t coff[2][2];
 #pragma unroll
@@ -252,14 +273,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
     if ((R) < 16) {                                                                         \
       const int ii_ = (R) >> 2, h_ = ((R) >> 1) & 1;                                        \
       const uint32_t b_ = base + (uint32_t)(((ur_ >> 1) & 1) * kBuf) + coff[ur_ & 1][h_];   \
-      if ((R) & 1) NB[ii_][h_] = lds_read16(b_ + b_off[ii_]);                               \
-      else NA[ii_][h_] = lds_read16(b_ + a_off[ii_]);                                       \
+      if ((R) & 1) NB[ii_][h_] = lds_read16_blk(b_ + b_off, ii_);                           \
+      else NA[ii_][h_] = lds_read16_blk(b_ + a_off, ii_);                                   \
     } else {                                                                                \
       const int jr_ = ur_ >> 1;                                                             \
       const uint32_t s_ = base + kScaleBase + (uint32_t)(mod3(jr_ >> 2) * kScaleSet) +      \
                           (uint32_t)((((jr_ & 3) + srot) & 3) * 4);                         \
-      if ((R) < 20) NSA[(R) - 16] = lds_read4(s_ + as_off[(R) - 16]);                       \
-      else NSB[(R) - 20] = lds_read4(s_ + bs_off[(R) - 20]);                                \
+      if ((R) < 20) NSA[(R) - 16] = lds_read4_blk(s_ + as_off, (R) - 16);                   \
+      else NSB[(R) - 20] = lds_read4_blk(s_ + bs_off, (R) - 20);                            \
     }                                                                                       \
   } while (0)
 
@@ -390,30 +411,43 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(acc[i][j][r], crow_p + j * 32);
         }
-    } else if (BF16 && full && (g.N & 1) == 0) {
+    } else if (BF16 && full && (g.N & 1) == 0 && g.N <= (1 << 22)) {
       // Registers r, r + 1 (r even) hold rows R, R + 1 of this lane's column.
       // The even lane of a pair stores columns (2c, 2c + 1) of row R, the odd
       // lane those of row R + 1.  Each lane rounds its two rows to one bf16
       // pair, swaps the pair with its partner, and one byte permute picks the
       // halves it stores: (own R, partner R) on the even lane, (partner R + 1,
-      // own R + 1) on the odd one.
+      // own R + 1) on the odd one.  Buffer stores over the tile: the lane's
+      // byte offset in one register, the row's in a scalar, the 32-column
+      // block's in the instruction (64-bit row pointers ran out of registers).
       const bool odd = (lane & 1) != 0;
       const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // bytes of {partner, own}
-      __bf16* cb = static_cast<__bf16*>(g.c) + (row0 + (odd ? 1 : 0)) * g.N + (col0 & ~(int64_t)1);
+      const uint32_t nb = (uint32_t)g.N * 2u;                  // bytes per row of C
+      const rsrc_t rc = make_rsrc(static_cast<__bf16*>(g.c) + em0 * g.N + en0, kTile * nb);
+      const uint32_t lane_off = (uint32_t)(wm * 128 + 4 * fh + (odd ? 1 : 0)) * nb +
+                                (uint32_t)(wn * 128 + (fr & ~1)) * 2u;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          __bf16* crow_p = cb + (int64_t)(i * 32 + (r & 3) + 8 * (r >> 2)) * g.N;
+          const int row_off = (i * 32 + (r & 3) + 8 * (r >> 2)) * (int)nb;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bf16x2 own = {(__bf16)acc[i][j][r], (__bf16)acc[i][j][r + 1]};
+            // read the two accumulators out of their AGPRs one at a time
+            // (left to itself the allocator keeps all 256 in VGPRs to feed the
+            // converts, and the rest of the kernel spills)
+            float lo, hi;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(lo) : "a"(acc[i][j][r]));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(hi) : "a"(acc[i][j][r + 1]));
+            const bf16x2 own = {(__bf16)lo, (__bf16)hi};
             const uint32_t ow = __builtin_bit_cast(uint32_t, own);
             const uint32_t pw = (uint32_t)__builtin_amdgcn_mov_dpp(
                 (int)ow, 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, true);
-            __builtin_nontemporal_store(__builtin_amdgcn_perm(pw, ow, sel),
-                                        reinterpret_cast<uint32_t*>(crow_p + j * 32));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(pw, ow, sel), rc,
+                                                  (int)(lane_off + 64u * j), row_off,
+                                                  2 /* nt */);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
     } else {
 #pragma unroll
@@ -425,10 +459,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_mx_gemm(const GemmArgs g) {
           for (int r = 0; r < 16; ++r) {
             const int64_t row = row0 + i * 32 + (r & 3) + 8 * (r >> 2);
             if (row < g.M && col < g.N) {
-              if (BF16) static_cast<__bf16*>(g.c)[row * g.N + col] = (__bf16)acc[i][j][r];
-              else static_cast<float*>(g.c)[row * g.N + col] = acc[i][j][r];
+              if (BF16) {
+                float v;  // read out of its AGPR on its own, as in the fast path
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[i][j][r]));
+                static_cast<__bf16*>(g.c)[row * g.N + col] = (__bf16)v;
+              } else {
+                static_cast<float*>(g.c)[row * g.N + col] = acc[i][j][r];
+              }
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
     }
     if (tile < 0) break;
