@@ -150,20 +150,23 @@ struct PowerSum {
 
 // rho = fl(c / r) * 2^shift, r = fl(fl(S)/K) (p = 1) or fl(sqrt(fl(fl(S)/K))),
 // shift = 40/p - (E1 - 127) (kSrcScales) or 24/p + 7 - (E1 - 127) (kSrcAbsmax).
-// Each step is one correctly rounded fp32 operation, evaluated in fp64 and
-// rounded once: a double result of +, *, /, sqrt on floats rounds to the
-// correctly rounded float (53 >= 2*24 + 2).  S * (1/K) in fp64 rounds to the
-// same float as S / K: a 24-bit S divided by K <= 2^10 is never within 2^-52 of
-// a float rounding boundary.  E1 == 255 (NaN/Inf in the row) gives NaN; S == 0
-// (an all-zero row, absmax reading) gives +Inf.
+// Each step is one correctly rounded fp32 operation.  fl(S/K) is evaluated
+// as S * (1/K) in fp64 and rounded once: the product is within 2^-53 of S/K
+// (1/K exact or correctly rounded), and a 24-bit S divided by K <= 2^10 is
+// never within 2^-52 of a float rounding boundary.  The square root and the
+// division are IEEE fp32 operations (the library is built with correctly
+// rounded fp32 divide and sqrt): shorter dependent chains than their fp64
+// forms, which the rows that arrive last in a launch wait on.  E1 == 255
+// (NaN/Inf in the row) gives NaN; S == 0 (an all-zero row, absmax reading)
+// gives +Inf.
 template <int SRC>
 __device__ __forceinline__ float rho_from_stat(int E1, double S, int p_shift, float c,
                                                double inv_k) {
   if (E1 >= 255) return __uint_as_float(0x7FC00000u);
   const float Sf = (float)S;  // exact in fp64 below 2^53; one rounding here
   const float mu = (float)((double)Sf * inv_k);
-  const float r = p_shift == 0 ? mu : (float)sqrt((double)mu);
-  const float q = (float)((double)c / (double)r);
+  const float r = p_shift == 0 ? mu : sqrtf(mu);
+  const float q = c / r;
   const int shift = SRC == kSrcScales ? (40 >> p_shift) - (E1 - 127)
                                       : (24 >> p_shift) + 7 - (E1 - 127);
   return (float)ldexp((double)q, shift);
