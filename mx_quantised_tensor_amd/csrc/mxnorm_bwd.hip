@@ -34,7 +34,8 @@
 //   * without a gain every wave takes one row (four per workgroup) up to
 //     hidden 2048; above that a row is split over 2 waves (as in the forward:
 //     measured at 16384 x 4096, 64.3 against 66.3 us with one wave per row --
-//     a wave's share of the last rows' work is half as long);
+//     a wave's share of the last rows' work is half as long), two rows per
+//     workgroup, and the last 4096 rows of a long launch over 4 waves each;
 //   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
 //     workgroup of W waves), lane `lane` of wave `wir` holding chunk
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
@@ -382,6 +383,58 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
   }
 }
 
+// Without a gain at 2048 < hidden <= 4096: workgroups of 4 waves carrying two
+// rows of 2 waves each, and, in launches of kBwdTailMinRows rows or more, the
+// last kBwdTailRows rows one per workgroup of 4 waves, so that each wave of
+// the launch's last dispatch round has half a row's work (measured against
+// one row of 2 waves per 128-thread workgroup: 16384 x 4096 62.96 against
+// 64.04 us, 32768 x 4096 125.7 against 128.8, 16384 x 3072 47.2 against
+// 48.9).  The waves of an empty row slot (an odd head row count) join the
+// row's barrier with no active chunk.
+constexpr int64_t kBwdTailRows = 4096;
+constexpr int64_t kBwdTailMinRows = 8192;
+
+__global__ __launch_bounds__(kBwdThreads) void k_mxnorm_bwd_pairs(const BwdArgs a,
+                                                                  int64_t head_blocks,
+                                                                  int64_t tail_rows) {
+  __shared__ float s_dot[8];  // head: 2 row slots x (2 parities x 2 waves); tail: 2 x 4
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunk = a.hidden >> 3;
+  float acc[1][8];  // no dgamma
+  const int64_t head_rows = a.rows - tail_rows;
+  if ((int64_t)blockIdx.x >= head_blocks) {
+    const int64_t row = head_rows + ((int64_t)blockIdx.x - head_blocks);
+    uint32_t choff[2];
+    bool act[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ch = (s * 4 + wave) * kWave + lane;
+      act[s] = ch < nchunk;
+      choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
+    }
+    uint4 xv[2], dv[2];
+    load_row<2>(a, row, choff, xv, dv);
+    bwd_row<false, 2, 4>(a, row, lane, choff, act, nullptr, xv, dv, acc, s_dot, wave, 0);
+    return;
+  }
+  const int rslot = wave >> 1, wir = wave & 1;
+  int64_t row = (int64_t)blockIdx.x * 2 + rslot;
+  const bool ok = row < head_rows;
+  if (!ok) row = 0;  // a valid row to read rho and x from; nothing is stored
+  uint32_t choff[4];
+  bool act[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int ch = (s * 2 + wir) * kWave + lane;
+    act[s] = ok && ch < nchunk;
+    choff[s] = (uint32_t)min(ch, nchunk - 1) * 16u;
+  }
+  uint4 xv[4], dv[4];
+  load_row<4>(a, row, choff, xv, dv);
+  bwd_row<false, 4, 2>(a, row, lane, choff, act, nullptr, xv, dv, acc, s_dot + rslot * 4, wir, 0);
+}
+
 // dgamma_j = sum over the G <= kBwdMaxPartials partial rows, in a fixed order.
 // Thread (slice, q) of a workgroup loads the float4 of columns 4q..4q+3 of
 // partial rows slice, slice + 32, ... (all loads issued before the adds; a
@@ -458,7 +511,13 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
   if (a.hidden > 8192) return launch_bwd_wide_t<GAMMA, 4>(a, groups, stream);
   if (a.hidden > 4096) return launch_bwd_wide_t<GAMMA, 2>(a, groups, stream);
   if constexpr (!GAMMA) {
-    if (a.hidden > 2048) return launch_bwd_wide_t<GAMMA, 2, 4>(a, groups, stream);
+    if (a.hidden > 2048) {
+      const int64_t tail = a.rows >= kBwdTailMinRows ? kBwdTailRows : 0;
+      const int64_t head_blocks = (a.rows - tail + 1) / 2;
+      hipLaunchKernelGGL(k_mxnorm_bwd_pairs, dim3((unsigned)(head_blocks + tail)),
+                         dim3(kBwdThreads), 0, (hipStream_t)stream, a, head_blocks, tail);
+      return hipGetLastError();
+    }
   }
   const int nchunk = a.hidden / 8;
   if (nchunk <= 64) return launch_bwd_t<GAMMA, 1>(a, groups, stream);

@@ -161,6 +161,28 @@ def test_bwd_maximum_rows_sampled():
     P.assert_bwd_close(got, None, xb, dyb, None, rho, ref_dx, None, "bwd max rows")
 
 
+@pytest.mark.parametrize("rows", [8191, 8192, 8193, 12289])
+@pytest.mark.parametrize("hidden", [3072, 4064, 4096])
+def test_bwd_no_gain_tail_part(rows, hidden):
+    # without a gain at 2048 < hidden <= 4096 rows go two per workgroup, and
+    # from 8192 rows on the last 4096 one per workgroup of 4 waves: the
+    # boundary between the parts, an odd head row count (an empty row slot),
+    # ragged widths, and zero / tiny rows placed in the tail part and across
+    # the boundary
+    xb, gb = W.generate(rows, hidden, "rowscale", rows + hidden)
+    xv = P.bf16_bits_to_f64(xb)
+    for r in (rows - 1, rows - 4096, rows - 4097):
+        if r >= 0:
+            xv[r] = 0.0
+    xv[rows - 2] *= 2.0 ** -50
+    xv[rows - 4098] *= 2.0 ** -120
+    xb = W.to_bf16_bits(xv.astype(np.float32))
+    dyb = W.grad_output(rows, hidden, rows)
+    _, _, rho = O.mxnorm_fwd(xb, gb, 2, C2, O.E4M3)
+    dxb, _ = _check(xb, dyb, None, rho, "no-gain tail rows=%d hidden=%d" % (rows, hidden))
+    assert np.isfinite(P.bf16_bits_to_f64(dxb)).all()
+
+
 @pytest.mark.parametrize("with_gamma", [True, False])
 @pytest.mark.parametrize("hidden", [512, 4096, 8192, 32768])
 def test_bwd_zero_and_tiny_rows(hidden, with_gamma):
