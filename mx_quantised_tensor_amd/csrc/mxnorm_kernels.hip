@@ -22,7 +22,8 @@
 //     against 28.9 us): a wave's cast is half as long, and the cast of the
 //     rows that arrive last is what the launch waits for at its end (with H16
 //     one wave per row stays faster); for the same reason the last 2048 rows
-//     of an E4M3 launch of 8192 rows or more are cast by 4 waves each;
+//     of an E4M3 launch of 8192 rows or more are cast by 4 waves each (at
+//     2048 columns, rows otherwise one per wave, the last 1536);
 //   * x is loaded and the codes stored non-temporally (each byte is touched
 //     once); the gain comes from L2, staged once per workgroup in LDS (by
 //     LDS-DMA loads as bf16, or widened to fp32 where that measured faster);
@@ -216,8 +217,8 @@ struct WaveArgs {
   uint8_t* scales;
   float* rrms;
   int scales_dwords;  // K % 4 == 0 and scales 4-byte aligned
-  int64_t head_blocks;  // k_mxnorm_wide: workgroups before the tail part
-  int64_t tail_rows;    // k_mxnorm_wide: rows of the tail part (at the end)
+  int64_t head_blocks;  // k_mxnorm_wide, k_mxnorm_wave_tail: workgroups before the tail part
+  int64_t tail_rows;    // the same kernels: rows of the tail part (at the end)
 };
 
 // Rows of up to 4 chunks per lane are widened to fp32 once, before the row
@@ -343,16 +344,17 @@ __device__ __forceinline__ void lane_chunks(int lane, int nchunk, bool (&act)[ST
 // barrier after they land.  Measured against requesting the whole gain into
 // VGPRs per wave, when this kernel still served 16384 x 4096 without rotation:
 // 34.0 against 34.6 us; H16 -> E2M1 at 32768 x 4096: 60.9 against 62.6 us.
+// Workgroup blk: rows 4 blk .. 4 blk + 3 of those below rlim.
 template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
-__global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+__device__ __forceinline__ void wave_rows(const WaveArgs& a, int64_t blk, int64_t rlim) {
   constexpr int NCH = STEPS * kWave;  // chunk slots of a row
   constexpr bool GF32 = WaveGain<STEPS>::F32;
   __shared__ uint32_t s_sc[4][STEPS * 4];  // the row's scale bytes, per wave
   __shared__ float4 s_gain[GAMMA ? WaveGain<STEPS>::kSlots : 1];  // layout: WaveGain
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  const bool row_ok = row < a.rows;  // waves past the end still stage the gain and meet the barrier
+  const int64_t row = blk * 4 + wave;
+  const bool row_ok = row < rlim;  // waves past the end still stage the gain and meet the barrier
 
   uint32_t choff[STEPS];  // byte offset of the lane's chunk (32-bit: SGPR row base)
   bool act[STEPS];
@@ -408,6 +410,11 @@ __global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
   }
   if (!row_ok) return;  // whole wave, after the only barrier
   wave_row<ELEM, GAMMA, HAD, STEPS, FULL, SRC>(a, row, lane, act, v, s_gain, s_sc[wave]);
+}
+
+template <int ELEM, bool GAMMA, int HAD, int STEPS, bool FULL, int SRC>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_wave(const WaveArgs a) {
+  wave_rows<ELEM, GAMMA, HAD, STEPS, FULL, SRC>(a, blockIdx.x, a.rows);
 }
 
 // ----------------------------------------------------------------------------------
@@ -913,6 +920,33 @@ __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const W
                                             s_sum, s_sc, s_gain);
 }
 
+// Rows of 2048 elements to E4M3 without rotation, in launches of
+// kWaveTailMinRows rows or more: k_mxnorm_wave's one wave per row (4 chunks
+// per lane), except for the last kWaveTailRows rows, each owned by a workgroup
+// of 4 waves (1 chunk per lane).  At 8192 rows every wave of the launch is
+// resident at once, and the launch ends on the statistic and cast of the rows
+// whose data arrive last, the last ones dispatched; there each wave then
+// casts a quarter as much.  Measured (same-process A/B, E4M3 with gain):
+// 8192 x 2048 9.77 against 10.15 us (without gain 9.74-9.85 against 10.05),
+// 16384 x 2048 17.53 against 17.86 us; tails of 768 and 2048 rows gained
+// less, 2 waves per tail row nothing, and at 4096 rows the tail was slower.
+constexpr int64_t kWaveTailRows = 1536;
+constexpr int64_t kWaveTailMinRows = 8192;
+
+template <int ELEM, bool GAMMA, int SRC>
+__global__ __launch_bounds__(kThreads) void k_mxnorm_wave_tail(const WaveArgs a) {
+  if ((int64_t)blockIdx.x >= a.head_blocks) {
+    __shared__ int s_max[4];
+    __shared__ double s_sum[4];
+    __shared__ uint32_t s_sc[4 * 4];
+    __shared__ uint4 s_gain[GAMMA ? 4 * kWave : 1];
+    wide_rows<ELEM, GAMMA, 0, 4, 1, SRC>(a, (int64_t)blockIdx.x - a.head_blocks,
+                                        a.rows - a.tail_rows, a.rows, s_max, s_sum, s_sc, s_gain);
+    return;
+  }
+  wave_rows<ELEM, GAMMA, 0, 4, true, SRC>(a, blockIdx.x, a.rows - a.tail_rows);
+}
+
 // ----------------------------------------------------------------------------------
 // MXCast of bf16 data ([P1] §1 and [P2] abstract: the cast whose block scales
 // MXNorm reuses).  Flat over 8-element chunks; a quad owns a block.
@@ -1086,7 +1120,17 @@ WaveArgs wave_args(const MxnormArgs& m) {
 
 template <int ELEM, bool GAMMA, int HAD, int SRC, int STEPS>
 hipError_t launch_wave(const MxnormArgs& m) {
-  const WaveArgs a = wave_args(m);
+  WaveArgs a = wave_args(m);
+  if constexpr (ELEM == 0 && HAD == 0 && STEPS == 4) {
+    if (m.hidden == 512 * STEPS && m.rows >= kWaveTailMinRows) {
+      a.tail_rows = kWaveTailRows;
+      a.head_blocks = (m.rows - a.tail_rows + 3) / 4;
+      hipLaunchKernelGGL((k_mxnorm_wave_tail<ELEM, GAMMA, SRC>),
+                         dim3((unsigned)(a.head_blocks + a.tail_rows)), dim3(kThreads), 0,
+                         (hipStream_t)m.stream, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)((m.rows + 3) / 4));
   if (m.hidden == 512 * STEPS)
     hipLaunchKernelGGL((k_mxnorm_wave<ELEM, GAMMA, HAD, STEPS, true, SRC>), grid,

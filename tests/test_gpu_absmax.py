@@ -60,6 +60,16 @@ def test_absmax_shapes(hidden, elem):
         _check(xb, None, p, 1.25, elem, what="D=%d p=%d no gamma" % (hidden, p))
 
 
+@pytest.mark.parametrize("rows", [8192, 8197])
+def test_absmax_wave_tail_part(rows):
+    # hidden 2048, E4M3, 8192 rows or more: the last 1536 rows are cast by
+    # workgroups of one row and 4 waves, with the exact block maxima as well
+    xb, gb = W.generate(rows, 2048, "rowscale", seed=rows + 3)
+    for p in (1, 2):
+        _check(xb, gb, p, C_ABS[p], 0, what="wave tail rows=%d p=%d" % (rows, p))
+    _check(xb, None, 2, 1.25, 0, what="wave tail rows=%d no gamma" % rows)
+
+
 @pytest.mark.parametrize("had", [16, 32])
 @pytest.mark.parametrize("hidden", [3072, 4096])
 @pytest.mark.parametrize("elem", [0, 1])

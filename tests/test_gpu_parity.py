@@ -196,6 +196,24 @@ def test_mxnorm_wide_tail_part(rows, hidden):
     _check_mxnorm(xb, None, 2, 10.0, 0, what="tail rows=%d D=%d no gamma" % (rows, hidden))
 
 
+@pytest.mark.parametrize("rows", [8191, 8192, 8193, 9999])
+def test_mxnorm_wave_tail_part(rows):
+    """E4M3 launches of 8192 rows or more at hidden 2048 (one wave per row)
+    hand their last 1536 rows to workgroups of one row and 4 waves: the
+    boundary between the two parts (row counts that leave the last 4-row
+    workgroup partly empty), 8191 rows (no tail part), and edge rows placed
+    in the tail part."""
+    hidden = 2048
+    xb, gb = W.generate(rows, hidden, "rowscale", seed=rows + 11)
+    e = _edge_rows(hidden)
+    xb[rows - 1 - len(e):rows - 1] = e          # in the tail part
+    xb[rows - 1536 - 3:rows - 1536 + 3] = e[:6]  # across the boundary
+    for p, c in ((2, C_DEF[2]), (1, 0.3)):
+        _check_mxnorm(xb, gb, p, c, 0, what="wave tail rows=%d p=%d" % (rows, p))
+    _check_mxnorm(xb, None, 2, 10.0, 0, what="wave tail rows=%d no gamma" % rows)
+    _check_mxnorm(xb, gb, 2, C_DEF[2], 1, what="wave tail rows=%d E2M1 (no tail)" % rows)
+
+
 def test_mxnorm_wide_tail_part_sampled():
     # a large E4M3 launch at hidden 4096 (the head part 292 K workgroups, then
     # 2048 one-row workgroups), checked on sampled rows the oracle computes one
