@@ -42,7 +42,8 @@ hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, 
 constexpr int kBwdMaxHidden = 32768;
 // Persistent workgroups of the backward with a gain, at most (one dgamma
 // partial row each): 512, 256 or 216 of 4 waves for rows of up to 1024, 2048
-// or 4096 elements; 512 of 2 waves, 256 of 4 or 8 waves for wider rows.
+// or 3584 elements; 256 of 8 waves for rows of 3585 to 4096 and 4609 to 8192;
+// 512 of 2 waves for 4097 to 4608; 256 of 4 or 8 waves for wider rows.
 constexpr int64_t kBwdMaxPartials = 512;
 
 struct BwdLaunch {
@@ -58,7 +59,6 @@ struct BwdLaunch {
   void* stream;
 };
 
-int bwd_waves_per_row(int hidden);
 int64_t bwd_groups(int64_t rows, int hidden);
 hipError_t launch_mxnorm_bwd(const BwdLaunch& l);
 

@@ -16,21 +16,21 @@
 //
 // Like the forward, this is an HBM-bound streaming pass (read x and dy, write
 // dx: 6 bytes per element); no dense contraction, no MFMA.
-//   * one wavefront owns a row at a time (hidden <= 4096) with the same lane
-//     layout as the forward: lane `lane` holds chunk s*64 + lane at step s;
+//   * one wavefront owns a row at a time (hidden <= 4096, except rows that
+//     nearly fill 4096 with a gain) with the same lane layout as the
+//     forward: lane `lane` holds chunk s*64 + lane at step s;
 //   * with a gain, waves are persistent over rows (row += total waves) so that
 //     each lane accumulates its columns' dgamma in registers across many
 //     rows, and each wave keeps the next row's loads in flight while it works
-//     on the current one.  At rows of 4096 only 216 workgroups of 4 waves
-//     run (864 waves, ~1700 rows in flight): measured on MI355X, more
-//     concurrent waves make this pattern slower (8 waves per CU: +18%; 3
-//     waves per SIMD: +14%), and 128 workgroups are too few; narrower rows,
-//     with fewer bytes in flight per wave, take up to 512 workgroups (see
-//     bwd_groups).  At the end the 4 waves of a workgroup
-//     add their accumulators through LDS in a fixed order and the workgroup
-//     writes one partial row; a second kernel adds the partial rows column
-//     by column in a fixed order.  Both orders depend only on (rows, hidden),
-//     so results are run-to-run reproducible;
+//     on the current one.  With one wave per row 216 workgroups of 4 waves
+//     run at rows of 3072 (864 waves): measured on MI355X, more concurrent
+//     waves make this pattern slower (8 waves per CU: +18%; 3 waves per SIMD:
+//     +14%), and 128 workgroups are too few; narrower rows, with fewer bytes
+//     in flight per wave, take up to 512 workgroups (see bwd_groups).  At the
+//     end the waves of a workgroup add their accumulators through LDS in a
+//     fixed order and the workgroup writes one partial row; a second kernel
+//     adds the partial rows column by column in a fixed order.  Both orders
+//     depend only on (rows, hidden), so results are run-to-run reproducible;
 //   * without a gain every wave takes one row (four per workgroup) up to
 //     hidden 2048; above that a row is split over 2 waves (as in the forward:
 //     measured at 16384 x 4096, 64.3 against 66.3 us with one wave per row --
@@ -41,8 +41,9 @@
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
 //     of y.g are added through LDS in wave order.  With a gain the workgroups
 //     are persistent over rows (512 of 2 waves, 256 of 4 or 8 waves: measured
-//     best); each wave owns distinct columns, so it writes its part of the
-//     workgroup's partial row directly.
+//     best), and rows that nearly fill 4096 or 8192 elements take 8 waves of
+//     1 or 2 steps (see gain_waves); each wave owns distinct columns, so it
+//     writes its part of the workgroup's partial row directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -309,8 +310,9 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
 }
 
 // Rows of up to 512 W STEPS elements: a workgroup of W waves owns one row at a
-// time (STEPS chunks per lane): 4096 < hidden <= 4096 W with 8 steps, and
-// without a gain 2048 < hidden <= 4096 with 2 waves of 4 steps.
+// time (STEPS chunks per lane): 4096 < hidden <= 4096 W with 8 steps; with a
+// gain rows that nearly fill 4096 or 8192 elements with 8 waves of 1 or 2
+// steps; without a gain 2048 < hidden <= 4096 with 2 waves of 4 steps.
 template <bool GAMMA, int W, bool FULL, int STEPS = 8>
 __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
 
   const int64_t stride = gridDim.x;
   int64_t row = blockIdx.x;
-  if constexpr (GAMMA && W == 8) {
+  if constexpr (GAMMA && W == 8 && STEPS == 8) {
     // 8 waves per workgroup leave 256 registers per wave: one register set
     // (the other waves of the SIMD keep loads in flight)
     int par = 0;
@@ -505,8 +507,35 @@ hipError_t launch_bwd_wide_t(const BwdArgs& a, int groups, void* stream) {
   return hipGetLastError();
 }
 
+// Waves per row of the backward with a gain (1: k_mxnorm_bwd; more:
+// k_mxnorm_bwd_wide).  Rows that nearly fill 4096 or 8192 elements take 8
+// waves of 1 or 2 steps, one 512-thread workgroup per CU.  Measured on MI355X
+// (same-process A/B, the partial-row sum included) against one wave per row
+// at 4096 and 2 waves of 8 steps at 8192: 16384 x 4096 67.4 against 71.4 us,
+// 8192 x 4096 36.6 against 41.2, 32768 x 4096 129.1 against 134.7, 16384 x
+// 3712 66.0 against 67.4, 8192 x 8192 69.0 against 76.9, 8192 x 6144 53.5
+// against 60.0, 8192 x 5120 50.5 against 51.2.  Narrower rows in each band
+// stream slower so (16384 x 3584 70.8 against 65.0 us, 16384 x 3072 66.4
+// against 57.9, 8192 x 4608 48.1 against 47.0), as do 128, 192, 384 or 512
+// workgroups, 4 waves of 2 steps at 8192 columns, a prefetch 2 or 3 rows
+// ahead, and 16 waves of 2 steps at 16384 columns (no gain there).
+int gain_waves(int hidden) {
+  if (hidden > 16384) return 8;  // 8 steps
+  if (hidden > 8192) return 4;   // 8 steps
+  if (hidden > 4608) return 8;   // 2 steps
+  if (hidden > 4096) return 2;   // 8 steps
+  if (hidden > 3584) return 8;   // 1 step
+  return 1;
+}
+
 template <bool GAMMA>
 hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
+  if constexpr (GAMMA) {
+    if (gain_waves(a.hidden) == 8 && a.hidden <= 4096)
+      return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
+    if (gain_waves(a.hidden) == 8 && a.hidden <= 8192)
+      return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+  }
   if (a.hidden > 16384) return launch_bwd_wide_t<GAMMA, 8>(a, groups, stream);
   if (a.hidden > 8192) return launch_bwd_wide_t<GAMMA, 4>(a, groups, stream);
   if (a.hidden > 4096) return launch_bwd_wide_t<GAMMA, 2>(a, groups, stream);
@@ -561,29 +590,25 @@ hipError_t bwd_scratch(int device, float** out) {
   return hipSuccess;
 }
 
-int bwd_waves_per_row(int hidden) {
-  return hidden > 16384 ? 8 : hidden > 8192 ? 4 : hidden > 4096 ? 2 : 1;
-}
-
 int64_t bwd_groups(int64_t rows, int hidden) {
-  const int w = bwd_waves_per_row(hidden);
+  const int w = gain_waves(hidden);
   if (w == 1) {
     // measured on MI355X with 4 waves per workgroup (the partial-row sum
     // included): rows of 512 or 1024 elements (1 or 2 chunks per lane, fewer
     // bytes in flight per wave) stream fastest with 512 workgroups (131072 x
     // 512: 68.5 against 101.5 us with 192; 65536 x 1024: 70.9 against 82.2),
     // rows of 2048 with 256 (16384 x 2048: 37.2 against 38.4), rows of 3072
-    // and 4096 with 216 (16384 x 4096: 71.8-72.0 against 72.6-73.2; 16384 x
-    // 3072: 57.9-58.2 against 60.4-60.9), where more concurrent rows stream
-    // slower (256: +3%)
+    // with 216 (16384 x 3072: 57.9-58.2 against 60.4-60.9; with one wave per
+    // row at 4096 too, 71.8-72.0 against 72.6-73.2), where more concurrent
+    // rows stream slower (256: +3%)
     const int nchunk = hidden / 8;
     const int64_t cap = nchunk <= 128 ? 512 : nchunk <= 256 ? 256 : 216;
     const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
     return need < cap ? need : cap;
   }
   // measured on MI355X at 16384 x 4096 / W rows (the partial-row sum included):
-  // 512 workgroups for W = 2, 256 for W = 4 and W = 8
-  const int64_t cap = w == 8 ? 256 : 1024 / w;
+  // 512 workgroups for W = 2, 256 for W = 4 and W = 8 (one per CU)
+  const int64_t cap = w == 2 ? 512 : 256;
   return rows < cap ? rows : cap;
 }
 

@@ -151,17 +151,22 @@ def test_bwd_workspace_size():
     assert ws(1, 64) == 64 * 4            # one workgroup
     assert ws(5, 64) == 2 * 64 * 4        # ceil(5 / 4) workgroups of 4 waves
     # one wave per row: 512, 256 and 216 workgroups at most for rows of up to
-    # 1024, 2048 and 4096 elements
-    assert ws(16384, 4096) == 216 * 4096 * 4
+    # 1024, 2048 and 3584 elements
+    assert ws(16384, 3584) == 216 * 3584 * 4
     assert ws(16384, 3072) == 216 * 3072 * 4
     assert ws(16384, 2048) == 256 * 2048 * 4
     assert ws(16384, 1024) == 512 * 1024 * 4
     assert ws(16384, 512) == 512 * 512 * 4
     assert ws(1000, 512) == 250 * 512 * 4
-    # wider rows: one row at a time per workgroup of W waves, 512 workgroups
-    # at most for W = 2 and 256 for W = 4, 8
+    # one row at a time per workgroup of W waves, 512 workgroups at most for
+    # W = 2 and 256 for W = 4, 8: rows that nearly fill 4096 or 8192 take 8
+    # waves, 4097 to 4608 take 2
+    assert ws(16384, 4096) == 256 * 4096 * 4      # W = 8, 1 step
+    assert ws(16384, 3616) == 256 * 3616 * 4
+    assert ws(16384, 4608) == 512 * 4608 * 4      # W = 2
+    assert ws(16384, 4640) == 256 * 4640 * 4      # W = 8, 2 steps
     assert ws(16, 8192) == 16 * 8192 * 4
-    assert ws(16384, 8192) == 512 * 8192 * 4      # W = 2
+    assert ws(16384, 8192) == 256 * 8192 * 4
     assert ws(16384, 12288) == 256 * 12288 * 4    # W = 4
     assert ws(16384, 32768) == 256 * 32768 * 4    # W = 8
     assert ws(16, 32800) == 0 and ws(16, 48) == 0 and ws(-1, 64) == 0
