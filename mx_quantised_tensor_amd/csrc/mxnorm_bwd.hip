@@ -43,7 +43,8 @@
 //     are persistent over rows (512 of 2 waves, 256 of 4 or 8 waves: measured
 //     best), and rows that nearly fill 4096 or 8192 elements take 8 waves of
 //     1 or 2 steps (see gain_waves); each wave owns distinct columns, so it
-//     writes its part of the workgroup's partial row directly.
+//     writes its part of the workgroup's partial row directly.  Without a
+//     gain, rows of 4097 to 8192 elements take 8 waves of 2 steps.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -310,9 +311,10 @@ __global__ __launch_bounds__(GAMMA ? kBwdWaves * 64 : kBwdThreads) void k_mxnorm
 }
 
 // Rows of up to 512 W STEPS elements: a workgroup of W waves owns one row at a
-// time (STEPS chunks per lane): 4096 < hidden <= 4096 W with 8 steps; with a
-// gain rows that nearly fill 4096 or 8192 elements with 8 waves of 1 or 2
-// steps; without a gain 2048 < hidden <= 4096 with 2 waves of 4 steps.
+// time (STEPS chunks per lane): 4096 < hidden <= 4096 W with 8 steps, except
+// rows of up to 8192 with 8 waves of 2 steps (with a gain those that nearly
+// fill 8192), and with a gain rows that nearly fill 4096 with 8 waves of 1
+// step; without a gain 2048 < hidden <= 4096 with 2 waves of 4 steps.
 template <bool GAMMA, int W, bool FULL, int STEPS = 8>
 __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -534,6 +536,14 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
     if (gain_waves(a.hidden) == 8 && a.hidden <= 4096)
       return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
     if (gain_waves(a.hidden) == 8 && a.hidden <= 8192)
+      return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+  } else {
+    // one row per 512-thread workgroup of 8 waves of 2 steps, measured on
+    // MI355X against 2 waves of 8 steps: 8192 x 8192 61.5 against 64.8 us,
+    // 8192 x 7168 54.8 against 58.3, 8192 x 4608 35.6 against 37.2 (4 waves
+    // of 4 steps in between); at 16384 and 32768 columns more waves with
+    // fewer steps measured the same or slower
+    if (a.hidden > 4096 && a.hidden <= 8192)
       return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
   }
   if (a.hidden > 16384) return launch_bwd_wide_t<GAMMA, 8>(a, groups, stream);
