@@ -32,10 +32,12 @@
 //     adds the partial rows column by column in a fixed order.  Both orders
 //     depend only on (rows, hidden), so results are run-to-run reproducible;
 //   * without a gain every wave takes one row (four per workgroup) up to
-//     hidden 2048; above that a row is split over 2 waves (as in the forward:
-//     measured at 16384 x 4096, 64.3 against 66.3 us with one wave per row --
-//     a wave's share of the last rows' work is half as long), two rows per
-//     workgroup, and the last 4096 rows of a long launch over 4 waves each;
+//     hidden 2048; above that (up to 4096, but see the wide rows below) a
+//     row is split over 2 waves (as in
+//     the forward: measured at 16384 x 4096, 64.3 against 66.3 us with one
+//     wave per row -- a wave's share of the last rows' work is half as long),
+//     two rows per workgroup, and the last 4096 rows of a long launch over 4
+//     waves each;
 //   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
 //     workgroup of W waves), lane `lane` of wave `wir` holding chunk
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
@@ -44,7 +46,9 @@
 //     best), and rows that nearly fill 4096 or 8192 elements take 8 waves of
 //     1 or 2 steps (see gain_waves); each wave owns distinct columns, so it
 //     writes its part of the workgroup's partial row directly.  Without a
-//     gain, rows of 4097 to 8192 elements take 8 waves of 2 steps.
+//     gain, rows of 3585 to 4096 elements (in launches of 16384 rows or more)
+//     take 8 waves of 1 step and rows of 4097 to 8192 8 waves of 2 steps,
+//     one row per workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -387,7 +391,8 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
   }
 }
 
-// Without a gain at 2048 < hidden <= 4096: workgroups of 4 waves carrying two
+// Without a gain at 2048 < hidden <= 4096 (except long launches of rows near
+// 4096, which take 8 waves per row): workgroups of 4 waves carrying two
 // rows of 2 waves each, and, in launches of kBwdTailMinRows rows or more, the
 // last kBwdTailRows rows one per workgroup of 4 waves, so that each wave of
 // the launch's last dispatch round has half a row's work (measured against
@@ -542,9 +547,15 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
     // MI355X against 2 waves of 8 steps: 8192 x 8192 61.5 against 64.8 us,
     // 8192 x 7168 54.8 against 58.3, 8192 x 4608 35.6 against 37.2 (4 waves
     // of 4 steps in between); at 16384 and 32768 columns more waves with
-    // fewer steps measured the same or slower
+    // fewer steps measured the same or slower.  Rows that nearly fill 4096,
+    // in launches of 16384 rows or more: 8 waves of 1 step (16384 x 4096
+    // 62.1-62.4 against 62.9-63.0 us with k_mxnorm_bwd_pairs, 32768 rows the
+    // same, 4 waves of 2 steps 63.4; at 8192 and 4096 rows the pairs are
+    // 0.5-1.4% faster, and at 3072 columns 0.1%)
     if (a.hidden > 4096 && a.hidden <= 8192)
       return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+    if (a.hidden > 3584 && a.hidden <= 4096 && a.rows >= 16384)
+      return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
   }
   if (a.hidden > 16384) return launch_bwd_wide_t<GAMMA, 8>(a, groups, stream);
   if (a.hidden > 8192) return launch_bwd_wide_t<GAMMA, 4>(a, groups, stream);

@@ -180,7 +180,7 @@ def test_bwd_maximum_rows_sampled():
 
 
 @pytest.mark.parametrize("rows", [8191, 8192, 8193, 12289])
-@pytest.mark.parametrize("hidden", [3072, 4064, 4096])
+@pytest.mark.parametrize("hidden", [2080, 3072, 3584, 4096])
 def test_bwd_no_gain_tail_part(rows, hidden):
     # without a gain at 2048 < hidden <= 4096 rows go two per workgroup, and
     # from 8192 rows on the last 4096 one per workgroup of 4 waves: the
@@ -198,6 +198,23 @@ def test_bwd_no_gain_tail_part(rows, hidden):
     dyb = W.grad_output(rows, hidden, rows)
     _, _, rho = O.mxnorm_fwd(xb, gb, 2, C2, O.E4M3)
     dxb, _ = _check(xb, dyb, None, rho, "no-gain tail rows=%d hidden=%d" % (rows, hidden))
+    assert np.isfinite(P.bf16_bits_to_f64(dxb)).all()
+
+
+@pytest.mark.parametrize("rows", [16383, 16384, 16385])
+@pytest.mark.parametrize("hidden", [3584, 3616, 4096])
+def test_bwd_no_gain_eight_waves_long_launch(rows, hidden):
+    # without a gain, launches of 16384 rows or more of 3585..4096 elements
+    # take one row per workgroup of 8 waves (16383 rows and 3584 columns:
+    # the pairs with their tail part); zero and tiny rows at the end
+    xb, _ = W.generate(rows, hidden, "rowscale", rows + 3 * hidden)
+    xv = P.bf16_bits_to_f64(xb)
+    xv[rows - 1] = 0.0
+    xv[rows - 2] *= 2.0 ** -120
+    xb = W.to_bf16_bits(xv.astype(np.float32))
+    dyb = W.grad_output(rows, hidden, rows + 1)
+    _, _, rho = O.mxnorm_fwd(xb, None, 2, C2, O.E4M3)
+    dxb, _ = _check(xb, dyb, None, rho, "no-gain long rows=%d hidden=%d" % (rows, hidden))
     assert np.isfinite(P.bf16_bits_to_f64(dxb)).all()
 
 
