@@ -32,12 +32,11 @@
 //     adds the partial rows column by column in a fixed order.  Both orders
 //     depend only on (rows, hidden), so results are run-to-run reproducible;
 //   * without a gain every wave takes one row (four per workgroup) up to
-//     hidden 2048; above that (up to 4096, but see the wide rows below) a
-//     row is split over 2 waves (as in
-//     the forward: measured at 16384 x 4096, 64.3 against 66.3 us with one
-//     wave per row -- a wave's share of the last rows' work is half as long),
-//     two rows per workgroup, and the last 4096 rows of a long launch over 4
-//     waves each;
+//     hidden 2048; above that (up to 4096, but see the wide rows below) a row
+//     is split over 2 waves (as in the forward: measured at 16384 x 4096,
+//     64.3 against 66.3 us with one wave per row -- a wave's share of the
+//     last rows' work is half as long), two rows per workgroup, and the last
+//     4096 rows of a long launch over 4 waves each;
 //   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
 //     workgroup of W waves), lane `lane` of wave `wir` holding chunk
 //     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
