@@ -23,8 +23,9 @@ per-call launch cost, which exceeds the kernel time of the small workloads):
     8192 x 2048 workload, and a rows sweep (8192 ... 65536 x 4096) of the
     kernel and the patterns with a least-squares fit t = a + bytes / B;
   * a device copy of the same byte count;
-  * the two-pass RMSNorm + MX cast baseline, the straight-through backward,
-    MXNormLinear (the MXFP8 matmul), the other workloads and the variants.
+  * the two-pass RMSNorm + MX cast baseline, the straight-through backward
+    (beside the backward's byte pattern at this shape), MXNormLinear (the
+    MXFP8 matmul), the other workloads and the variants.
 
 `python bench.py --counters NAME` only runs one kernel 20 times and a 256 MiB
 device copy (the calibration of the HBM byte counters), for rocprofv3 --pmc;
@@ -486,6 +487,28 @@ def main():
                     key += "_%dx%d" % (br, bh)
                 extras[key + "_us_per_call"] = round(us, 3)
                 extras[key + "_algorithmic_GBps"] = round(bwd_bytes(br, bh, gain) / us / 1e3, 1)
+            if br == rows:
+                # the backward's byte pattern (libmxq_measure.so: x and dy read,
+                # dx written, each store waiting for its whole row) in the
+                # backward's layouts, 2 and 8 waves per row
+                pats = {}
+                for wv in (2, 8):
+                    if not M.mxq_bwd_pattern_supported(wv, bh):
+                        continue
+                    pc = [lambda st, s=s, wv=wv: M.mxq_measure_bwd_pattern(
+                        wv, s["x"].data_ptr(), s["dy"].data_ptr(), br, bh, s["dx"].data_ptr(), st)
+                        for s in bsets]
+                    us = graph_us(pc, 100)
+                    pats["waves_%d" % wv] = {"us": round(us, 3),
+                                             "GBps": round(bwd_bytes(br, bh, False) / us / 1e3, 1)}
+                if pats:
+                    best = min(v["us"] for v in pats.values())
+                    extras["bwd_patterns_%dx%d" % (br, bh)] = pats
+                    extras["bwd_best_pattern_frac_of_peak"] = round(
+                        bwd_bytes(br, bh, False) / best / 1e3 / PEAK_HBM_GBS, 4)
+                    for key in ("mxnorm_bwd", "mxnorm_bwd_no_gain"):
+                        extras[key + "_over_best_bwd_pattern"] = round(
+                            extras[key + "_us_per_call"] / best, 4)
             del bsets
             torch.cuda.empty_cache()
 

@@ -48,6 +48,29 @@ int mxq_pattern_supported(int layout, int64_t hidden);
 int mxq_measure_pattern(int layout, const void *x, int64_t rows, int64_t hidden, uint8_t *codes,
                         uint8_t *scales, float *rrms, void *stream);
 
+/*
+ * The backward's byte pattern: the bytes of an mxnorm_bwd call without a
+ * gain ([P1] "Resumen tecnico" §2, gradients item of "Implementacion": the
+ * straight-through backward reads x and dy and writes dx), 16-byte
+ * non-temporal loads of x [rows, hidden] and dy [rows, hidden] (bf16) and
+ * non-temporal 16-byte stores of dx [rows, hidden] (bf16), no arithmetic
+ * beyond XOR.  Output: F = XOR of every 32-bit word of the row's x and dy;
+ * every 32-bit word of dx is the matching x word ^ dy word ^ F.  `waves`
+ * waves own a row (2: two rows per 256-thread workgroup; 8: one row per
+ * 512-thread workgroup), with the backward's lane layout.
+ */
+
+/* mxq_bwd_pattern_supported -- host: 1 if waves is 2 or 8 and hidden =
+ * waves * 512 * {1, 2, 4, 8}, else 0. */
+int mxq_bwd_pattern_supported(int waves, int64_t hidden);
+
+/* mxq_measure_bwd_pattern -- enqueue one backward pattern pass on `stream`.
+ * x, dy, dx: 16-byte aligned device pointers.  Returns 0 on success, -1 bad
+ * argument, -2 misaligned pointer, -3 unsupported waves/shape, -4 launch
+ * failure.  rows == 0 is a no-op. */
+int mxq_measure_bwd_pattern(int waves, const void *x, const void *dy, int64_t rows,
+                            int64_t hidden, void *dx, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

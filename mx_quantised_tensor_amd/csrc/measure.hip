@@ -23,6 +23,15 @@
 //               + 64 + lane), then neighbouring lanes swap halves by DPP so a
 //               lane holds a whole 16-element group, one 16-byte code store.
 // W waves own a row (4/W rows per 256-thread workgroup).
+//
+// The backward's byte pattern (mxq_measure_bwd_pattern): reads x and dy
+// [rows, hidden] bf16 and writes dx [rows, hidden] bf16, the bytes of an
+// mxnorm_bwd call without a gain, with the backward's lane layout (lane `lane`
+// of wave `wir` holds chunk (wir*NCH + s)*64 + lane of x and of dy) over 2
+// waves per row (two rows per 256-thread workgroup) or 8 (one row per
+// 512-thread workgroup).  F is the XOR of every 32-bit word of the row's x
+// and dy (no dx store leaves before the whole row has arrived, as the
+// backward's row dot); each 16-byte dx chunk is the word-wise x ^ dy ^ F.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -135,6 +144,66 @@ __global__ __launch_bounds__(256) void k_pattern(const uint8_t* __restrict__ x, 
   if (wir == 0 && lane == 0) rrms[row] = __uint_as_float(f);
 }
 
+template <int W, int NCH>
+__global__ __launch_bounds__(W > 4 ? W * 64 : 256) void k_bwd_pattern(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ dy, int64_t rows,
+    uint8_t* __restrict__ dx) {
+  constexpr int NW = W > 4 ? W : 4;  // waves per workgroup
+  constexpr int RPW = NW / W;
+  constexpr int HID = W * kWave * 8 * NCH;
+  __shared__ uint32_t s_f[NW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rslot = wave / W, wir = wave % W;
+  const int64_t row = (int64_t)blockIdx.x * RPW + rslot;
+  const bool row_ok = row < rows;  // waves past the end still meet the barrier
+  const int64_t base = (row_ok ? row : 0) * (int64_t)HID * 2;
+  uint4 a[NCH], b[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t ch = (uint32_t)((wir * NCH + c) * kWave + lane);
+    a[c] = load_nt(x + base + ch * 16u);
+    b[c] = load_nt(dy + base + ch * 16u);
+  }
+  uint32_t f = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    f ^= a[c].x ^ a[c].y ^ a[c].z ^ a[c].w ^ b[c].x ^ b[c].y ^ b[c].z ^ b[c].w;
+  f = wave_xor(f);
+  if (lane == 0) s_f[wave] = f;
+  __syncthreads();
+  f = s_f[rslot * W];
+#pragma unroll
+  for (int w = 1; w < W; ++w) f ^= s_f[rslot * W + w];
+  if (!row_ok) return;
+  uint8_t* drow = dx + row * (int64_t)HID * 2;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t ch = (uint32_t)((wir * NCH + c) * kWave + lane);
+    const u32x4_t o = {a[c].x ^ b[c].x ^ f, a[c].y ^ b[c].y ^ f, a[c].z ^ b[c].z ^ f,
+                       a[c].w ^ b[c].w ^ f};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(drow + ch * 16u));
+  }
+}
+
+template <int W>
+hipError_t launch_bwd(const void* x, const void* dy, int64_t rows, int hidden, void* dx,
+                      hipStream_t st) {
+  constexpr int NW = W > 4 ? W : 4, RPW = NW / W;
+  const dim3 grid((unsigned)((rows + RPW - 1) / RPW)), block(NW * kWave);
+  const uint8_t* xp = static_cast<const uint8_t*>(x);
+  const uint8_t* dp = static_cast<const uint8_t*>(dy);
+  uint8_t* op = static_cast<uint8_t*>(dx);
+  switch (hidden / (W * kWave * 8)) {
+    case 1: hipLaunchKernelGGL((k_bwd_pattern<W, 1>), grid, block, 0, st, xp, dp, rows, op); break;
+    case 2: hipLaunchKernelGGL((k_bwd_pattern<W, 2>), grid, block, 0, st, xp, dp, rows, op); break;
+    case 4: hipLaunchKernelGGL((k_bwd_pattern<W, 4>), grid, block, 0, st, xp, dp, rows, op); break;
+    case 8: hipLaunchKernelGGL((k_bwd_pattern<W, 8>), grid, block, 0, st, xp, dp, rows, op); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int W, int NCH, int MODE>
 hipError_t launch(const void* x, int64_t rows, uint8_t* codes, uint8_t* scales, float* rrms,
                   hipStream_t st) {
@@ -198,6 +267,28 @@ int mxq_measure_pattern(int layout, const void* x, int64_t rows, int64_t hidden,
     case MXQ_PATTERN_TWO_WAVES_LANE16: e = launch_hidden<2, kLane16>(x, rows, h, codes, scales, rrms, st); break;
     default: break;
   }
+  return e == hipSuccess ? 0 : -4;
+}
+
+int mxq_bwd_pattern_supported(int waves, int64_t hidden) {
+  if (waves != 2 && waves != 8) return 0;
+  if (hidden <= 0 || hidden % (waves * kWave * 8) != 0) return 0;
+  const int64_t nch = hidden / (waves * kWave * 8);
+  return nch == 1 || nch == 2 || nch == 4 || nch == 8;
+}
+
+int mxq_measure_bwd_pattern(int waves, const void* x, const void* dy, int64_t rows,
+                            int64_t hidden, void* dx, void* stream) {
+  if (rows < 0 || hidden <= 0) return -1;
+  if (!mxq_bwd_pattern_supported(waves, hidden)) return -3;
+  if (rows > ((int64_t)1 << 24) - 1) return -3;
+  if (rows == 0) return 0;
+  if (x == nullptr || dy == nullptr || dx == nullptr) return -1;
+  if (((uintptr_t)x & 15) || ((uintptr_t)dy & 15) || ((uintptr_t)dx & 15)) return -2;
+  (void)hipGetLastError();
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = waves == 2 ? launch_bwd<2>(x, dy, rows, (int)hidden, dx, st)
+                                  : launch_bwd<8>(x, dy, rows, (int)hidden, dx, st);
   return e == hipSuccess ? 0 : -4;
 }
 

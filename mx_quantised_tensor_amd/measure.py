@@ -34,5 +34,10 @@ def lib():
         L.mxq_measure_pattern.restype = C.c_int
         L.mxq_measure_pattern.argtypes = [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
                                           C.c_void_p, C.c_void_p, C.c_void_p]
+        L.mxq_bwd_pattern_supported.restype = C.c_int
+        L.mxq_bwd_pattern_supported.argtypes = [C.c_int, C.c_int64]
+        L.mxq_measure_bwd_pattern.restype = C.c_int
+        L.mxq_measure_bwd_pattern.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_int64,
+                                              C.c_int64, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib

@@ -287,7 +287,8 @@ def test_measure_library_exports_and_checks():
     text = open(os.path.join(ROOT, "include", "mxq_measure.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, re.M))
-    assert names == {"mxq_pattern_supported", "mxq_measure_pattern"}
+    assert names == {"mxq_pattern_supported", "mxq_measure_pattern", "mxq_bwd_pattern_supported",
+                     "mxq_measure_bwd_pattern"}
     M = measure.lib()
     for n in names:
         assert hasattr(M, n), n
@@ -307,6 +308,18 @@ def test_measure_library_exports_and_checks():
     assert f(x=None) == EINVAL
     assert f(x=MIS) == EALIGN
     assert f(scales=A16 + 2) == EALIGN
+    bsup = lambda w, h: M.mxq_bwd_pattern_supported(w, h)
+    assert bsup(2, 4096) and bsup(8, 4096) and bsup(2, 1024) and bsup(8, 32768)
+    assert not bsup(1, 4096) and not bsup(4, 4096) and not bsup(8, 2048) and not bsup(2, 3072)
+    assert not bsup(2, 16384) and not bsup(8, 0)
+    bf = lambda **kw: M.mxq_measure_bwd_pattern(kw.get("w", 8), kw.get("x", A16), kw.get("dy", A16),
+                                                kw.get("rows", 4), kw.get("hidden", 4096),
+                                                kw.get("dx", A16), None)
+    assert bf(w=4) == EUNSUP and bf(hidden=3072) == EUNSUP and bf(rows=1 << 24) == EUNSUP
+    assert bf(rows=-1) == EINVAL and bf(hidden=0) == EINVAL
+    assert bf(rows=0, x=None, dy=None, dx=None) == OK
+    assert bf(dy=None) == EINVAL and bf(dx=None) == EINVAL
+    assert bf(x=MIS) == EALIGN and bf(dy=A16 + 8) == EALIGN and bf(dx=A16 + 4) == EALIGN
 
 
 def test_bwd_noalloc_argument_checks_and_scratch_size():

@@ -376,6 +376,28 @@ def test_measure_patterns_move_the_bytes(layout, hidden):
     assert np.array_equal(rr.cpu().numpy().view(np.uint32), f)
 
 
+@pytest.mark.parametrize("waves,hidden", [(2, 4096), (8, 4096), (8, 8192), (2, 1024)])
+def test_measure_bwd_pattern_moves_the_bytes(waves, hidden):
+    # the backward's byte pattern reads every word of x and dy and writes
+    # every word of dx: check its XOR outputs on the host
+    from mx_quantised_tensor_amd import measure
+    M = measure.lib()
+    rows = 37
+    rng = np.random.default_rng(7 + waves + hidden)
+    xw = rng.integers(0, 2 ** 32, size=(rows, hidden // 2), dtype=np.uint32)
+    dw = rng.integers(0, 2 ** 32, size=(rows, hidden // 2), dtype=np.uint32)
+    x = torch.from_numpy(xw.view(np.int32)).cuda()
+    dy = torch.from_numpy(dw.view(np.int32)).cuda()
+    dx = torch.empty_like(x)
+    print("case: backward pattern %d waves hidden %d" % (waves, hidden), flush=True)
+    st = M.mxq_measure_bwd_pattern(waves, x.data_ptr(), dy.data_ptr(), rows, hidden,
+                                   dx.data_ptr(), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    f = np.bitwise_xor.reduce(xw, axis=1) ^ np.bitwise_xor.reduce(dw, axis=1)
+    assert np.array_equal(dx.cpu().numpy().view(np.uint32), xw ^ dw ^ f[:, None])
+
+
 def test_mxnorm_maximum_rows_sampled():
     # the largest row count the C ABI accepts (2^24 - 1: the grid then holds
     # 2^22 workgroups), hidden 64, checked on sampled rows that the oracle
