@@ -41,9 +41,10 @@ hipError_t launch_mx_quant_gain(const void* w, const void* gamma, int64_t rows, 
 // Straight-through MXNorm backward.  hidden <= kBwdMaxHidden.
 constexpr int kBwdMaxHidden = 32768;
 // Persistent workgroups of the backward with a gain, at most (one dgamma
-// partial row each): 512, 256 or 216 of 4 waves for rows of up to 1024, 2048
-// or 3584 elements; 256 of 8 waves for rows of 3585 to 4096 and 4609 to 8192;
-// 512 of 2 waves for 4097 to 4608; 256 of 4 or 8 waves for wider rows.
+// partial row each): 512 or 256 of 4 waves for rows of up to 1024 or 2048
+// elements (one wave per row); then 512 of 5 waves (up to 2560), 512 of 3
+// (3072), 256 of 7 (3584), 256 of 8 (4096), 512 of 2 (4608), 256 of 8
+// (8192), 256 of 4 or 8 for wider rows.
 constexpr int64_t kBwdMaxPartials = 512;
 
 struct BwdLaunch {

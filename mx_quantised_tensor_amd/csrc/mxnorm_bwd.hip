@@ -16,37 +16,36 @@
 //
 // Like the forward, this is an HBM-bound streaming pass (read x and dy, write
 // dx: 6 bytes per element); no dense contraction, no MFMA.
-//   * one wavefront owns a row at a time (hidden <= 4096, except rows that
-//     nearly fill 4096 with a gain) with the same lane layout as the
-//     forward: lane `lane` holds chunk s*64 + lane at step s;
+//   * one wavefront owns a row at a time (up to hidden 2048 with a gain, 4096
+//     without) with the same lane layout as the forward: lane `lane` holds
+//     chunk s*64 + lane at step s;
 //   * with a gain, waves are persistent over rows (row += total waves) so that
 //     each lane accumulates its columns' dgamma in registers across many
 //     rows, and each wave keeps the next row's loads in flight while it works
-//     on the current one.  With one wave per row 216 workgroups of 4 waves
-//     run at rows of 3072 (864 waves): measured on MI355X, more concurrent
-//     waves make this pattern slower (8 waves per CU: +18%; 3 waves per SIMD:
-//     +14%), and 128 workgroups are too few; narrower rows, with fewer bytes
-//     in flight per wave, take up to 512 workgroups (see bwd_groups).  At the
-//     end the waves of a workgroup add their accumulators through LDS in a
-//     fixed order and the workgroup writes one partial row; a second kernel
-//     adds the partial rows column by column in a fixed order.  Both orders
-//     depend only on (rows, hidden), so results are run-to-run reproducible;
+//     on the current one.  With one wave per row, 256 or 512 workgroups of 4
+//     waves (more concurrent waves made this pattern slower: 8 waves per CU
+//     +18%, 3 waves per SIMD +14%; 128 workgroups are too few; see
+//     bwd_groups).  At the end the waves of a workgroup add their
+//     accumulators through LDS in a fixed order and the workgroup writes one
+//     partial row; a second kernel adds the partial rows column by column in
+//     a fixed order.  Both orders depend only on (rows, hidden), so results
+//     are run-to-run reproducible;
 //   * without a gain every wave takes one row (four per workgroup) up to
 //     hidden 2048; above that (up to 4096, but see the wide rows below) a row
 //     is split over 2 waves (as in the forward: measured at 16384 x 4096,
 //     64.3 against 66.3 us with one wave per row -- a wave's share of the
 //     last rows' work is half as long), two rows per workgroup, and the last
 //     4096 rows of a long launch over 4 waves each;
-//   * rows wider than 4096 (up to 32768) are owned by W = 2, 4 or 8 waves (a
-//     workgroup of W waves), lane `lane` of wave `wir` holding chunk
-//     (s*W + wir)*64 + lane at step s, as in the wide forward; the W wave sums
-//     of y.g are added through LDS in wave order.  With a gain the workgroups
-//     are persistent over rows (512 of 2 waves, 256 of 4 or 8 waves: measured
-//     best), and rows that nearly fill 4096 or 8192 elements take 8 waves of
-//     1 or 2 steps (see gain_waves); each wave owns distinct columns, so it
-//     writes its part of the workgroup's partial row directly.  Without a
-//     gain, rows of 3585 to 4096 elements (in launches of 16384 rows or more)
-//     take 8 waves of 1 step and rows of 4097 to 8192 8 waves of 2 steps,
+//   * rows of more waves (k_mxnorm_bwd_wide): lane `lane` of wave `wir` holds
+//     chunk (s*W + wir)*64 + lane at step s, as in the wide forward; the W
+//     wave sums of y.g are added through LDS in wave order.  With a gain,
+//     rows of 2049 to 4096 elements take 3 to 8 waves of 1 or 2 steps, wider
+//     rows 2, 4 or 8 waves (8 of 2 steps up to 8192), over persistent
+//     workgroups, one or two per CU (see gain_layout, bwd_groups); each wave
+//     owns distinct columns, so it writes its part of the workgroup's
+//     partial row directly.  Without a gain, rows of 3585 to 4096 elements
+//     (in launches of 16384 rows or more) take 8 waves of 1 step, rows of
+//     4097 to 8192 8 waves of 2 steps, wider rows 4 or 8 waves of 8 steps,
 //     one row per workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -513,34 +512,47 @@ hipError_t launch_bwd_wide_t(const BwdArgs& a, int groups, void* stream) {
   return hipGetLastError();
 }
 
-// Waves per row of the backward with a gain (1: k_mxnorm_bwd; more:
-// k_mxnorm_bwd_wide).  Rows that nearly fill 4096 or 8192 elements take 8
-// waves of 1 or 2 steps, one 512-thread workgroup per CU.  Measured on MI355X
-// (same-process A/B, the partial-row sum included) against one wave per row
-// at 4096 and 2 waves of 8 steps at 8192: 16384 x 4096 67.4 against 71.4 us,
-// 8192 x 4096 36.6 against 41.2, 32768 x 4096 129.1 against 134.7, 16384 x
-// 3712 66.0 against 67.4, 8192 x 8192 69.0 against 76.9, 8192 x 6144 53.5
-// against 60.0, 8192 x 5120 50.5 against 51.2.  Narrower rows in each band
-// stream slower so (16384 x 3584 70.8 against 65.0 us, 16384 x 3072 66.4
-// against 57.9, 8192 x 4608 48.1 against 47.0), as do 128, 192, 384 or 512
-// workgroups, 4 waves of 2 steps at 8192 columns, a prefetch 2 or 3 rows
-// ahead, and 16 waves of 2 steps at 16384 columns (no gain there).
-int gain_waves(int hidden) {
-  if (hidden > 16384) return 8;  // 8 steps
-  if (hidden > 8192) return 4;   // 8 steps
-  if (hidden > 4608) return 8;   // 2 steps
-  if (hidden > 4096) return 2;   // 8 steps
-  if (hidden > 3584) return 8;   // 1 step
-  return 1;
+// Row layout of the backward with a gain: `waves` waves of `steps` chunks
+// per lane own a row (1 wave: k_mxnorm_bwd, its steps set by the width; more:
+// k_mxnorm_bwd_wide).  From 2049 to 4096 elements and from 4609 to 8192, few
+// steps over many waves: a row's loads and its dot are spread over more
+// waves, and the persistent workgroups (one or two per CU, see bwd_groups)
+// keep 6 to 10 waves per CU.  Measured on MI355X (same-process A/B, the
+// partial-row sum included) against one wave of 4 or 8 steps per row up to
+// 4096 and 2 waves of 8 steps at 8192: 16384 x 2336 45.8 against 49.0 us,
+// 16384 x 2560 46.3 against 50.6, 16384 x 3072 53.7 against 57.8 (6 waves
+// of 1 step: 54.7), 16384 x 3584 60.7 against 65.3, 16384 x 3712 66.0
+// against 67.4, 16384 x 4096 67.4 against 71.4, 8192 x 4096 36.6 against
+// 41.2, 32768 x 4096 129.1 against 134.7, 8192 x 5120 50.5 against 51.2,
+// 8192 x 6144 53.5 against 60.0, 8192 x 8192 69.0 against 76.9.  At 2048
+// columns (4 waves of 1 step: +1.5-32%) and from 4097 to 4608 (8 waves of 2
+// steps: +2.7%) the older layouts stay; a prefetch 2 or 3 rows ahead, 4
+// waves of 2 steps at 8192 columns and 16 waves of 2 steps at 16384 measured
+// slower or the same.
+struct GainLayout {
+  int waves, steps;
+};
+GainLayout gain_layout(int hidden) {
+  if (hidden > 16384) return {8, 8};
+  if (hidden > 8192) return {4, 8};
+  if (hidden > 4608) return {8, 2};
+  if (hidden > 4096) return {2, 8};
+  if (hidden > 3584) return {8, 1};
+  if (hidden > 3072) return {7, 1};
+  if (hidden > 2560) return {3, 2};
+  if (hidden > 2048) return {5, 1};
+  return {1, 0};
 }
 
 template <bool GAMMA>
 hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
   if constexpr (GAMMA) {
-    if (gain_waves(a.hidden) == 8 && a.hidden <= 4096)
-      return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
-    if (gain_waves(a.hidden) == 8 && a.hidden <= 8192)
-      return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+    const GainLayout gl = gain_layout(a.hidden);
+    if (gl.waves == 5) return launch_bwd_wide_t<GAMMA, 5, 1>(a, groups, stream);
+    if (gl.waves == 3) return launch_bwd_wide_t<GAMMA, 3, 2>(a, groups, stream);
+    if (gl.waves == 7) return launch_bwd_wide_t<GAMMA, 7, 1>(a, groups, stream);
+    if (gl.waves == 8 && gl.steps == 1) return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
+    if (gl.waves == 8 && gl.steps == 2) return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
   } else {
     // one row per 512-thread workgroup of 8 waves of 2 steps, measured on
     // MI355X against 2 waves of 8 steps: 8192 x 8192 61.5 against 64.8 us,
@@ -611,24 +623,26 @@ hipError_t bwd_scratch(int device, float** out) {
 }
 
 int64_t bwd_groups(int64_t rows, int hidden) {
-  const int w = gain_waves(hidden);
+  const int w = gain_layout(hidden).waves;
   if (w == 1) {
     // measured on MI355X with 4 waves per workgroup (the partial-row sum
     // included): rows of 512 or 1024 elements (1 or 2 chunks per lane, fewer
     // bytes in flight per wave) stream fastest with 512 workgroups (131072 x
     // 512: 68.5 against 101.5 us with 192; 65536 x 1024: 70.9 against 82.2),
-    // rows of 2048 with 256 (16384 x 2048: 37.2 against 38.4), rows of 3072
-    // with 216 (16384 x 3072: 57.9-58.2 against 60.4-60.9; with one wave per
-    // row at 4096 too, 71.8-72.0 against 72.6-73.2), where more concurrent
-    // rows stream slower (256: +3%)
+    // rows of 2048 with 256 (16384 x 2048: 37.2 against 38.4); when rows of
+    // 3072 and 4096 ran one wave per row, 216 (16384 x 3072: 57.9-58.2
+    // against 60.4-60.9; 16384 x 4096: 71.8-72.0 against 72.6-73.2)
     const int nchunk = hidden / 8;
     const int64_t cap = nchunk <= 128 ? 512 : nchunk <= 256 ? 256 : 216;
     const int64_t need = (rows + kBwdWaves - 1) / kBwdWaves;
     return need < cap ? need : cap;
   }
-  // measured on MI355X at 16384 x 4096 / W rows (the partial-row sum included):
-  // 512 workgroups for W = 2, 256 for W = 4 and W = 8 (one per CU)
-  const int64_t cap = w == 2 ? 512 : 256;
+  // measured on MI355X (the partial-row sum included): 512 workgroups (two
+  // per CU) for 2, 3 and 5 waves per row, 256 (one per CU) for 4, 7 and 8
+  // (16384 x 2560 with 5 waves: 46.3 against 52.2 us with 256; 16384 x 3072
+  // with 3 waves: 53.7 against 61.1; 16384 x 3584 with 7 waves: 60.7 against
+  // 64.4 with 512)
+  const int64_t cap = (w == 2 || w == 3 || w == 5) ? 512 : 256;
   return rows < cap ? rows : cap;
 }
 

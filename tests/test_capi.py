@@ -150,17 +150,21 @@ def test_bwd_workspace_size():
     assert ws(0, 4096) == 0
     assert ws(1, 64) == 64 * 4            # one workgroup
     assert ws(5, 64) == 2 * 64 * 4        # ceil(5 / 4) workgroups of 4 waves
-    # one wave per row: 512, 256 and 216 workgroups at most for rows of up to
-    # 1024, 2048 and 3584 elements
-    assert ws(16384, 3584) == 216 * 3584 * 4
-    assert ws(16384, 3072) == 216 * 3072 * 4
+    # one wave per row: 512 and 256 workgroups at most for rows of up to 1024
+    # and 2048 elements
     assert ws(16384, 2048) == 256 * 2048 * 4
     assert ws(16384, 1024) == 512 * 1024 * 4
     assert ws(16384, 512) == 512 * 512 * 4
     assert ws(1000, 512) == 250 * 512 * 4
     # one row at a time per workgroup of W waves, 512 workgroups at most for
-    # W = 2 and 256 for W = 4, 8: rows that nearly fill 4096 or 8192 take 8
-    # waves, 4097 to 4608 take 2
+    # W = 2, 3, 5 and 256 for W = 4, 7, 8: rows of 2049..2560 take 5 waves,
+    # 2561..3072 3, 3073..3584 7, 3585..4096 8, 4097..4608 2, 4609..8192 8
+    assert ws(16384, 2080) == 512 * 2080 * 4      # W = 5, 1 step
+    assert ws(16384, 2560) == 512 * 2560 * 4
+    assert ws(16384, 2592) == 512 * 2592 * 4      # W = 3, 2 steps
+    assert ws(16384, 3072) == 512 * 3072 * 4
+    assert ws(16384, 3104) == 256 * 3104 * 4      # W = 7, 1 step
+    assert ws(16384, 3584) == 256 * 3584 * 4
     assert ws(16384, 4096) == 256 * 4096 * 4      # W = 8, 1 step
     assert ws(16384, 3616) == 256 * 3616 * 4
     assert ws(16384, 4608) == 512 * 4608 * 4      # W = 2

@@ -78,13 +78,16 @@ def test_bwd_wide_rows_persistent(hidden):
 
 
 @pytest.mark.parametrize("with_gamma", [True, False])
-@pytest.mark.parametrize("hidden", [3584, 3616, 3712, 4000, 4096, 4608, 4640, 5120, 7168, 8192])
-def test_bwd_eight_wave_bands(hidden, with_gamma):
-    # with a gain, rows of 3585..4096 and 4609..8192 elements take 8 waves of
-    # 1 or 2 steps over 256 persistent workgroups (3584 and 4608: the layouts
-    # on either side); without one, rows of 4097..8192 take 8 waves of 2
-    # steps, one row per workgroup; row counts below, at and above the
-    # persistent grid, ragged last steps, and the same bits from a second run
+@pytest.mark.parametrize("hidden", [2048, 2080, 2336, 2560, 2592, 3072, 3104, 3584, 3616, 3712,
+                                    4000, 4096, 4608, 4640, 5120, 7168, 8192])
+def test_bwd_multi_wave_bands(hidden, with_gamma):
+    # with a gain, rows of 2049..2560 elements take 5 waves of 1 step,
+    # 2561..3072 3 waves of 2 steps, 3073..3584 7 waves of 1 step,
+    # 3585..4096 8 waves of 1 step and 4609..8192 8 waves of 2 steps, over
+    # 256 or 512 persistent workgroups (2048 and 4608: the layouts beside
+    # them); without one, rows of 4097..8192 take 8 waves of 2 steps, one row
+    # per workgroup; row counts below, at and above the persistent grid,
+    # ragged last steps, and the same bits from a second run
     for rows in (1, 255, 257, 700):
         xb, dyb, gb, rho = _inputs(rows, hidden, kind="rowscale", seed=hidden + 7 * rows,
                                    with_gamma=with_gamma)
