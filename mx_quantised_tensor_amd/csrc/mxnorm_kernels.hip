@@ -802,11 +802,12 @@ __device__ __forceinline__ void wide_rows(const WaveArgs& a, int64_t blk, int64_
   if constexpr (GAMMA) {
     const rsrc_t rg = row_rsrc(a.gamma, (uint32_t)a.hidden * 2u);
 #pragma unroll
-    for (int j = 0; j < W * STEPS / NW; ++j) {
-      const int grp = j * NW + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + grp * kWave * 16), 16,
-          (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
+    for (int j = 0; j < (W * STEPS + NW - 1) / NW; ++j) {
+      const int grp = j * NW + wave;  // W STEPS groups of 64 chunks in all
+      if ((W * STEPS) % NW == 0 || grp < W * STEPS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (MXQ_LDS void*)((MXQ_LDS uint8_t*)s_gain + grp * kWave * 16), 16,
+            (int)((uint32_t)(grp * kWave + lane) * 16u), 0, 0, 0);
     }
   }
   const uint8_t* xrow = a.x + (row_ok ? row : 0) * (int64_t)a.hidden * 2;
@@ -1178,11 +1179,13 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
   if (r.waves == 1 && r.steps == 2) return launch_wave<ELEM, GAMMA, HAD, SRC, 2>(m);
   if (r.waves == 1 && r.steps == 4) return launch_wave<ELEM, GAMMA, HAD, SRC, 4>(m);
   if (r.waves == 1 && r.steps == 8) {
-    // 2048 < hidden <= 4096: 2 waves per row, except with a rotation (its
-    // longer cast per element runs faster one wave per row); on rows of
-    // exactly 4096, E2M1 rotations with a whole 32-group per lane, H32 and
-    // H16 with a gain to E4M3 with whole 16-groups per lane
+    // 2048 < hidden <= 4096: 2 waves per row of 3 or 4 steps (as many as
+    // the width needs), except with a rotation (its longer cast per element
+    // runs faster one wave per row); on rows of exactly 4096, E2M1 rotations
+    // with a whole 32-group per lane, H32 and H16 with a gain to E4M3 with
+    // whole 16-groups per lane
     if constexpr (HAD == 0) {
+      if (m.hidden <= 3072) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 3>(m);
       return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 4>(m);
     } else {
       if constexpr (SRC == kSrcScales && ELEM == 1) {
@@ -1194,7 +1197,22 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
       return launch_wave<ELEM, GAMMA, HAD, SRC, 8>(m);
     }
   }
-  if (r.waves == 2 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
+  if (r.waves == 2 && r.steps == 8) {
+    // 4096 < hidden <= 8192: 2 waves of as many steps as the width needs (a
+    // lane's chunks past the row end still cost their clamped loads and
+    // masks).  Measured against 8 steps (and 4 at 2048 < hidden <= 3072), E4M3
+    // with gain: 8192 x 4608 21.0 against 21.9 us, 8192 x 5120 23.0 against
+    // 23.8, 8192 x 6144 27.1 against 27.5, 8192 x 7168 31.2 against 31.5,
+    // 16384 x 2336 21.8 against 22.5, 16384 x 2560 22.2 against 22.8, 16384 x
+    // 3072 25.6 against 25.9 (E2M1 21.6 against 22.1); H16 -> E2M1 at 8192 x
+    // 6144 25.1 against 26.1
+    switch ((m.hidden / 8 + 2 * kWave - 1) / (2 * kWave)) {
+      case 5: return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 5>(m);
+      case 6: return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 6>(m);
+      case 7: return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 7>(m);
+      default: return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
+    }
+  }
   if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
   // the table's 4 x 16 entry (rows above 16384) runs here as 8 waves of 8 steps,
   // one 512-thread workgroup per row: half the registers per wave, and 3% faster
