@@ -1213,11 +1213,28 @@ hipError_t launch_mxnorm_shape(const MxnormArgs& m) {
       default: return launch_wide<ELEM, GAMMA, HAD, SRC, 2, 8>(m);
     }
   }
-  if (r.waves == 4 && r.steps == 8) return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
-  // the table's 4 x 16 entry (rows above 16384) runs here as 8 waves of 8 steps,
-  // one 512-thread workgroup per row: half the registers per wave, and 3% faster
-  // at 32768 elements with gain
-  if (r.waves == 4 && r.steps == 16) return launch_wide<ELEM, GAMMA, HAD, SRC, 8, 8>(m);
+  // wider rows likewise: 8192 < hidden <= 16384 on 4 waves of 5 to 8 steps
+  // (4096 x 10240 24.1 against 26.1 us with 8 steps, 4096 x 12288 28.3
+  // against 28.9); the table's 4 x 16 entry (rows above 16384) on 8 waves of
+  // 5 to 8 steps, one 512-thread workgroup per row (half the registers per
+  // wave of 4 x 16, and 3% faster at 32768 elements with gain; 2048 x 20480
+  // 24.8 against 29.4 us with 8 steps, 2048 x 24576 29.1 against 31.2)
+  if (r.waves == 4 && r.steps == 8) {
+    switch ((m.hidden / 8 + 4 * kWave - 1) / (4 * kWave)) {
+      case 5: return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 5>(m);
+      case 6: return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 6>(m);
+      case 7: return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 7>(m);
+      default: return launch_wide<ELEM, GAMMA, HAD, SRC, 4, 8>(m);
+    }
+  }
+  if (r.waves == 4 && r.steps == 16) {
+    switch ((m.hidden / 8 + 8 * kWave - 1) / (8 * kWave)) {
+      case 5: return launch_wide<ELEM, GAMMA, HAD, SRC, 8, 5>(m);
+      case 6: return launch_wide<ELEM, GAMMA, HAD, SRC, 8, 6>(m);
+      case 7: return launch_wide<ELEM, GAMMA, HAD, SRC, 8, 7>(m);
+      default: return launch_wide<ELEM, GAMMA, HAD, SRC, 8, 8>(m);
+    }
+  }
   return hipErrorInvalidValue;
 }
 

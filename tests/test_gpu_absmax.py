@@ -51,7 +51,7 @@ def test_absmax_workloads_full(cfg, p):
 
 
 @pytest.mark.parametrize("hidden", [32, 96, 768, 1056, 2592, 3104, 4096, 4128, 5152, 7168, 8192,
-                                    32768])
+                                    10272, 20480, 32768])
 @pytest.mark.parametrize("elem", [0, 1])
 def test_absmax_shapes(hidden, elem):
     rows = 37 if hidden <= 8192 else 5

@@ -112,7 +112,8 @@ def test_mxnorm_workloads_full(cfg, p):
 
 @pytest.mark.parametrize("hidden", [32, 64, 96, 160, 512, 768, 1056, 2048, 2080, 2560, 2592, 3072,
                                     3104, 4064, 4096, 4128, 5120, 5152, 6144, 6176, 7168, 7200,
-                                    8192, 12288, 16384, 32768])
+                                    8192, 10240, 10272, 12288, 14336, 16384, 20480, 20512,
+                                    24576, 28672, 28704, 32768])
 @pytest.mark.parametrize("elem", [0, 1])
 def test_mxnorm_shapes(hidden, elem):
     rows = 67 if hidden <= 8192 else 9
@@ -289,7 +290,7 @@ def test_mxnorm_deterministic_and_side_stream():
 
 @pytest.mark.parametrize("had", [16, 32])
 @pytest.mark.parametrize("elem", [1, 0])
-@pytest.mark.parametrize("hidden", [32, 96, 768, 3072, 4096, 5120, 6176, 8192])
+@pytest.mark.parametrize("hidden", [32, 96, 768, 3072, 4096, 5120, 6176, 8192, 10240, 24576])
 def test_hadamard_shapes(had, elem, hidden):
     xb, gb = W.generate(41, hidden, "outlier", seed=had + hidden)
     _check_mxnorm(xb, gb, 2, C_DEF[2], elem, had=had, what="H%d D=%d" % (had, hidden))
