@@ -553,6 +553,19 @@ hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
     if (gl.waves == 7) return launch_bwd_wide_t<GAMMA, 7, 1>(a, groups, stream);
     if (gl.waves == 8 && gl.steps == 1) return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
     if (gl.waves == 8 && gl.steps == 2) return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+    // above 8192 elements, 4 or 8 waves of as many steps as the width needs
+    // (4096 x 10240 49.5 against 54.9 us with 8 steps, 4096 x 12288 58.7
+    // against 61.9, 2048 x 20480 55.2 against 59.7, 2048 x 24576 64.8 against
+    // 67.5; without a gain 0.2-1% faster or 2.5% slower, so it keeps 8)
+    if (gl.steps == 8 && (gl.waves == 4 || gl.waves == 8)) {
+      const int steps = (a.hidden / 8 + gl.waves * kWave - 1) / (gl.waves * kWave);
+      if (gl.waves == 4 && steps == 5) return launch_bwd_wide_t<GAMMA, 4, 5>(a, groups, stream);
+      if (gl.waves == 4 && steps == 6) return launch_bwd_wide_t<GAMMA, 4, 6>(a, groups, stream);
+      if (gl.waves == 4 && steps == 7) return launch_bwd_wide_t<GAMMA, 4, 7>(a, groups, stream);
+      if (gl.waves == 8 && steps == 5) return launch_bwd_wide_t<GAMMA, 8, 5>(a, groups, stream);
+      if (gl.waves == 8 && steps == 6) return launch_bwd_wide_t<GAMMA, 8, 6>(a, groups, stream);
+      if (gl.waves == 8 && steps == 7) return launch_bwd_wide_t<GAMMA, 8, 7>(a, groups, stream);
+    }
   } else {
     // one row per 512-thread workgroup of 8 waves of 2 steps, measured on
     // MI355X against 2 waves of 8 steps: 8192 x 8192 61.5 against 64.8 us,

@@ -58,19 +58,23 @@ def test_bwd_shapes(hidden, with_gamma):
 
 
 @pytest.mark.parametrize("with_gamma", [True, False])
-@pytest.mark.parametrize("hidden", [4128, 6144, 8192, 8224, 12288, 16384, 20480, 32768])
+@pytest.mark.parametrize("hidden", [4128, 6144, 8192, 8224, 10240, 10272, 12288, 14336, 16384,
+                                    16416, 20480, 20512, 24576, 28672, 28704, 32768])
 def test_bwd_wide_rows(hidden, with_gamma):
-    # 2, 4 or 8 waves per row, full and ragged last steps
+    # 2, 4 or 8 waves per row, full and ragged last steps; with a gain, rows
+    # above 8192 elements take 5 to 8 steps per wave as the width needs
+    # (8224 and 16416: 5 steps with a ragged last one, 10272 and 20512: 6,
+    # 14336 and 28672: 7 full ones, 28704: 8)
     for rows in (1, 5, 67):
         xb, dyb, gb, rho = _inputs(rows, hidden, with_gamma=with_gamma, seed=hidden + rows)
         _check(xb, dyb, gb, rho, "rows=%d hidden=%d gamma=%s" % (rows, hidden, with_gamma))
 
 
-@pytest.mark.parametrize("hidden", [8192, 16384, 32768])
+@pytest.mark.parametrize("hidden", [8192, 10240, 16384, 24576, 32768])
 def test_bwd_wide_rows_persistent(hidden):
     # more rows than workgroups (512 or 256 of them): each workgroup takes several
     # rows, alternating register sets (W = 2, 4) or one set (W = 8)
-    rows = {8192: 1200, 16384: 600, 32768: 600}[hidden]
+    rows = {8192: 1200, 10240: 600, 16384: 600, 24576: 600, 32768: 600}[hidden]
     xb, dyb, gb, rho = _inputs(rows, hidden, kind="rowscale", seed=hidden)
     dx1, dg1 = _check(xb, dyb, gb, rho, "persistent rows=%d hidden=%d" % (rows, hidden))
     dx2, dg2 = _run(xb, dyb, gb, rho)
