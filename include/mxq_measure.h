@@ -32,7 +32,8 @@ enum {
     MXQ_PATTERN_ONE_WAVE_LANE16 = 2,   /* lane: 16 consecutive elements (loads 16 B apart), 16-byte stores */
     MXQ_PATTERN_ONE_WAVE_LANE16X = 3,  /* contiguous loads, a DPP swap of halves, 16-byte stores */
     MXQ_PATTERN_TWO_WAVES_LANE16 = 4,  /* two waves, 16 consecutive elements per lane */
-    MXQ_PATTERN_COUNT = 5
+    MXQ_PATTERN_TWO_WAVES_LANE16X = 5, /* two waves, each a contiguous half; loads and stores as 3 */
+    MXQ_PATTERN_COUNT = 6
 };
 
 /* mxq_pattern_supported -- host: 1 if `layout` covers rows of `hidden`

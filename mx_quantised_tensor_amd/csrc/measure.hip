@@ -237,7 +237,8 @@ extern "C" {
 int mxq_pattern_supported(int layout, int64_t hidden) {
   if (layout < 0 || layout >= MXQ_PATTERN_COUNT) return 0;
   const int waves = (layout == MXQ_PATTERN_TWO_WAVES_CHUNK8 ||
-                     layout == MXQ_PATTERN_TWO_WAVES_LANE16) ? 2 : 1;
+                     layout == MXQ_PATTERN_TWO_WAVES_LANE16 ||
+                     layout == MXQ_PATTERN_TWO_WAVES_LANE16X) ? 2 : 1;
   const int min_chunks = (layout == MXQ_PATTERN_ONE_WAVE_CHUNK8 ||
                           layout == MXQ_PATTERN_TWO_WAVES_CHUNK8) ? 1 : 2;
   if (hidden <= 0 || hidden % (waves * kWave * 8) != 0) return 0;
@@ -265,6 +266,7 @@ int mxq_measure_pattern(int layout, const void* x, int64_t rows, int64_t hidden,
     case MXQ_PATTERN_ONE_WAVE_LANE16: e = launch_hidden<1, kLane16>(x, rows, h, codes, scales, rrms, st); break;
     case MXQ_PATTERN_ONE_WAVE_LANE16X: e = launch_hidden<1, kLane16X>(x, rows, h, codes, scales, rrms, st); break;
     case MXQ_PATTERN_TWO_WAVES_LANE16: e = launch_hidden<2, kLane16>(x, rows, h, codes, scales, rrms, st); break;
+    case MXQ_PATTERN_TWO_WAVES_LANE16X: e = launch_hidden<2, kLane16X>(x, rows, h, codes, scales, rrms, st); break;
     default: break;
   }
   return e == hipSuccess ? 0 : -4;

@@ -9,9 +9,10 @@ TWO_WAVES_CHUNK8 = 1
 ONE_WAVE_LANE16 = 2
 ONE_WAVE_LANE16X = 3
 TWO_WAVES_LANE16 = 4
+TWO_WAVES_LANE16X = 5
 LAYOUTS = {ONE_WAVE_CHUNK8: "one_wave_chunk8", TWO_WAVES_CHUNK8: "two_waves_chunk8",
            ONE_WAVE_LANE16: "one_wave_lane16", ONE_WAVE_LANE16X: "one_wave_lane16x",
-           TWO_WAVES_LANE16: "two_waves_lane16"}
+           TWO_WAVES_LANE16: "two_waves_lane16", TWO_WAVES_LANE16X: "two_waves_lane16x"}
 
 _PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmxq_measure.so")
 _lib = None

@@ -300,7 +300,8 @@ def test_measure_library_exports_and_checks():
     sup = lambda lay, h: M.mxq_pattern_supported(lay, h)
     assert sup(0, 4096) and sup(1, 4096) and sup(2, 4096) and sup(3, 4096) and sup(4, 4096)
     assert sup(0, 512) and not sup(2, 512) and not sup(1, 512) and sup(1, 1024)
-    assert not sup(4, 1024) and sup(4, 2048) and not sup(0, 768) and not sup(5, 4096)
+    assert not sup(4, 1024) and sup(4, 2048) and not sup(0, 768) and sup(5, 4096)
+    assert not sup(5, 1024) and sup(5, 2048) and not sup(6, 4096)
     f = lambda **kw: M.mxq_measure_pattern(kw.get("lay", 0), kw.get("x", A16), kw.get("rows", 4),
                                            kw.get("hidden", 4096), kw.get("codes", A16),
                                            kw.get("scales", A16), kw.get("rrms", A16), None)

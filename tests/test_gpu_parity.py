@@ -346,7 +346,7 @@ def test_baseline_shapes(hidden, elem):
     _check_baseline(xb, None, 0.0, elem, "two-pass D=%d no gamma" % hidden)
 
 
-@pytest.mark.parametrize("layout", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("layout", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("hidden", [2048, 4096])
 def test_measure_patterns_move_the_bytes(layout, hidden):
     # every byte-pattern reference reads every input word and writes every
