@@ -39,9 +39,11 @@
 //   * rows of more waves (k_mxnorm_bwd_wide): lane `lane` of wave `wir` holds
 //     chunk (s*W + wir)*64 + lane at step s, as in the wide forward; the W
 //     wave sums of y.g are added through LDS in wave order.  With a gain,
-//     rows of 2049 to 4096 elements take 3 to 8 waves of 1 or 2 steps, wider
-//     rows 2, 4 or 8 waves (8 of 2 steps up to 8192), over persistent
-//     workgroups, one or two per CU (see gain_layout, bwd_groups); each wave
+//     rows of 2049 to 4096 elements take 3 to 8 waves of 1 or 2 steps, rows
+//     of 4097 to 4608 2 waves of 8 steps, rows up to 8192 8 waves of 2 steps,
+//     wider rows 4 waves (up to 16384) or 8 of as many steps (5 to 8) as the
+//     width needs, over persistent workgroups, one or two per CU (see
+//     gain_layout, bwd_groups); each wave
 //     owns distinct columns, so it writes its part of the workgroup's
 //     partial row directly.  Without a gain, rows of 3585 to 4096 elements
 //     (in launches of 16384 rows or more) take 8 waves of 1 step, rows of
@@ -528,13 +530,19 @@ hipError_t launch_bwd_wide_t(const BwdArgs& a, int groups, void* stream) {
 // columns (4 waves of 1 step: +1.5-32%) and from 4097 to 4608 (8 waves of 2
 // steps: +2.7%) the older layouts stay; a prefetch 2 or 3 rows ahead, 4
 // waves of 2 steps at 8192 columns and 16 waves of 2 steps at 16384 measured
-// slower or the same.
+// slower or the same.  Above 8192 elements, 4 waves (up to 16384) or 8 of
+// as many steps as the width needs (5 to 8) against 8 steps: 4096 x 10240
+// 49.5 against 54.9 us, 4096 x 12288 58.7 against 61.9, 2048 x 20480 55.2
+// against 59.7, 2048 x 24576 64.8 against 67.5 (without a gain the same fit
+// measured 0.2-1% faster or 2.5% slower, so those rows keep 8 steps).
 struct GainLayout {
   int waves, steps;
 };
 GainLayout gain_layout(int hidden) {
-  if (hidden > 16384) return {8, 8};
-  if (hidden > 8192) return {4, 8};
+  if (hidden > 8192) {
+    const int w = hidden > 16384 ? 8 : 4;
+    return {w, (hidden / 8 + w * kWave - 1) / (w * kWave)};  // 5 to 8 steps
+  }
   if (hidden > 4608) return {8, 2};
   if (hidden > 4096) return {2, 8};
   if (hidden > 3584) return {8, 1};
@@ -548,23 +556,20 @@ template <bool GAMMA>
 hipError_t launch_bwd_steps(const BwdArgs& a, int groups, void* stream) {
   if constexpr (GAMMA) {
     const GainLayout gl = gain_layout(a.hidden);
-    if (gl.waves == 5) return launch_bwd_wide_t<GAMMA, 5, 1>(a, groups, stream);
-    if (gl.waves == 3) return launch_bwd_wide_t<GAMMA, 3, 2>(a, groups, stream);
-    if (gl.waves == 7) return launch_bwd_wide_t<GAMMA, 7, 1>(a, groups, stream);
-    if (gl.waves == 8 && gl.steps == 1) return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
-    if (gl.waves == 8 && gl.steps == 2) return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
-    // above 8192 elements, 4 or 8 waves of as many steps as the width needs
-    // (4096 x 10240 49.5 against 54.9 us with 8 steps, 4096 x 12288 58.7
-    // against 61.9, 2048 x 20480 55.2 against 59.7, 2048 x 24576 64.8 against
-    // 67.5; without a gain 0.2-1% faster or 2.5% slower, so it keeps 8)
-    if (gl.steps == 8 && (gl.waves == 4 || gl.waves == 8)) {
-      const int steps = (a.hidden / 8 + gl.waves * kWave - 1) / (gl.waves * kWave);
-      if (gl.waves == 4 && steps == 5) return launch_bwd_wide_t<GAMMA, 4, 5>(a, groups, stream);
-      if (gl.waves == 4 && steps == 6) return launch_bwd_wide_t<GAMMA, 4, 6>(a, groups, stream);
-      if (gl.waves == 4 && steps == 7) return launch_bwd_wide_t<GAMMA, 4, 7>(a, groups, stream);
-      if (gl.waves == 8 && steps == 5) return launch_bwd_wide_t<GAMMA, 8, 5>(a, groups, stream);
-      if (gl.waves == 8 && steps == 6) return launch_bwd_wide_t<GAMMA, 8, 6>(a, groups, stream);
-      if (gl.waves == 8 && steps == 7) return launch_bwd_wide_t<GAMMA, 8, 7>(a, groups, stream);
+    // {1, 0}, {2, 8}, {4, 8} and {8, 8} take the generic launches below
+    switch (gl.waves * 16 + gl.steps) {
+      case 5 * 16 + 1: return launch_bwd_wide_t<GAMMA, 5, 1>(a, groups, stream);
+      case 3 * 16 + 2: return launch_bwd_wide_t<GAMMA, 3, 2>(a, groups, stream);
+      case 7 * 16 + 1: return launch_bwd_wide_t<GAMMA, 7, 1>(a, groups, stream);
+      case 8 * 16 + 1: return launch_bwd_wide_t<GAMMA, 8, 1>(a, groups, stream);
+      case 8 * 16 + 2: return launch_bwd_wide_t<GAMMA, 8, 2>(a, groups, stream);
+      case 4 * 16 + 5: return launch_bwd_wide_t<GAMMA, 4, 5>(a, groups, stream);
+      case 4 * 16 + 6: return launch_bwd_wide_t<GAMMA, 4, 6>(a, groups, stream);
+      case 4 * 16 + 7: return launch_bwd_wide_t<GAMMA, 4, 7>(a, groups, stream);
+      case 8 * 16 + 5: return launch_bwd_wide_t<GAMMA, 8, 5>(a, groups, stream);
+      case 8 * 16 + 6: return launch_bwd_wide_t<GAMMA, 8, 6>(a, groups, stream);
+      case 8 * 16 + 7: return launch_bwd_wide_t<GAMMA, 8, 7>(a, groups, stream);
+      default: break;
     }
   } else {
     // one row per 512-thread workgroup of 8 waves of 2 steps, measured on
