@@ -261,8 +261,8 @@ mxq_status mxnorm_linear_fwd(const void *x, int64_t rows, int64_t hidden, int p,
  * above).  The sum over a row of y.g: per lane, eight fused multiply-add
  * chains (one per position in the lane's 8-element chunks, over the chunks in
  * order) added in a fixed tree, then a fixed tree over the wave, and where
- * a row is split over 2, 4 or 8 waves (with a gain, rows wider than 3584;
- * without one, rows wider than 2048) the wave sums added in wave order.
+ * a row is split over several waves (2 to 8, rows wider than 2048; the
+ * count depends only on rows and hidden) the wave sums added in wave order.
  * Two launches with a gain (rows, then the dgamma column sums), one without.
  */
 mxq_status mxnorm_bwd(const void *x, const void *dy, const void *gamma, const float *rrms,
