@@ -891,27 +891,35 @@ __device__ __forceinline__ void wide_rows(const WaveArgs& a, int64_t blk, int64_
 }
 
 
-// Rows per launch that k_mxnorm_wide<2 waves, 4 steps> hands, at the end of
-// the grid, to workgroups owning one row with 4 waves (E4M3 only).  The launch
-// ends on the row statistic and cast of the rows whose data arrive last; in
-// the last dispatch round (2048 rows = 8192 waves) each wave then casts half
+// Rows per launch that k_mxnorm_wide<2 waves, 4 to 8 steps> hands, at the end
+// of the grid, to workgroups owning one row with 4 waves of half as many steps
+// (E4M3 only).  The launch ends on the row statistic and cast of the rows
+// whose data arrive last; in the last dispatch round each wave then casts half
 // as much.  Measured at hidden 4096, E4M3 with gain: 8192 rows 17.91 against
 // 18.52 us, 16384 rows 32.99 against 33.54 us, 32768 rows 63.73 against 64.37
 // us, 65536 rows within noise; E2M1 (a shorter cast per element) was slower.
+// 8192 rows of 4608 to 8192 elements: 20.4-20.6 against 21.0 us at 4608,
+// 22.3-22.5 against 23.0 at 5120, 26.3-26.4 against 27.0-27.1 at 6144,
+// 30.5-30.6 against 31.2-31.3 at 7168, 33.9-34.0 against 34.8 at 8192
+// (16384 rows: 0.5-1% faster); 3-step rows (2049 to 3072 elements) gained
+// nothing at 3072 and lost 1.4-2.5% at 2336 and 2560, so they keep none.
 constexpr int64_t kWideTailRows = 2048;
 constexpr int64_t kWideTailMinRows = 8192;
 
 template <int ELEM, bool GAMMA, int HAD, int W, int STEPS, int SRC>
 __global__ __launch_bounds__((W > 4 ? W : 4) * kWave) void k_mxnorm_wide(const WaveArgs a) {
   constexpr int NW = W > 4 ? W : 4;
+  constexpr bool kTail = ELEM == 0 && W == 2 && STEPS >= 4;
+  constexpr int TS = (STEPS + 1) / 2;  // steps per lane of the tail part's 4 waves
+  constexpr int kGainSlots = kTail && 4 * TS > W * STEPS ? 4 * TS * kWave : W * STEPS * kWave;
   __shared__ int s_max[NW];
   __shared__ double s_sum[NW];
-  __shared__ uint32_t s_sc[NW * STEPS * 4];
-  __shared__ uint4 s_gain[GAMMA ? W * STEPS * kWave : 1];
-  if constexpr (ELEM == 0 && W == 2 && STEPS == 4) {
-    // the tail part: same LDS footprint (4 waves x 2 steps of the same row width)
+  __shared__ uint32_t s_sc[NW * STEPS * 4];  // the tail part's NW * TS * 4 fit
+  __shared__ uint4 s_gain[GAMMA ? kGainSlots : 1];
+  if constexpr (kTail) {
+    // the tail part: 4 waves of (STEPS + 1) / 2 steps over the same row width
     if ((int64_t)blockIdx.x >= a.head_blocks) {
-      wide_rows<ELEM, GAMMA, HAD, 4, 2, SRC>(a, (int64_t)blockIdx.x - a.head_blocks,
+      wide_rows<ELEM, GAMMA, HAD, 4, TS, SRC>(a, (int64_t)blockIdx.x - a.head_blocks,
                                             a.rows - a.tail_rows, a.rows, s_max, s_sum, s_sc,
                                             s_gain);
       return;
@@ -1146,7 +1154,7 @@ template <int ELEM, bool GAMMA, int HAD, int SRC, int W, int STEPS>
 hipError_t launch_wide(const MxnormArgs& m) {
   WaveArgs a = wave_args(m);
   constexpr int NW = W > 4 ? W : 4, RPW = NW / W;
-  a.tail_rows = (ELEM == 0 && W == 2 && STEPS == 4 && m.rows >= kWideTailMinRows) ? kWideTailRows : 0;
+  a.tail_rows = (ELEM == 0 && W == 2 && STEPS >= 4 && m.rows >= kWideTailMinRows) ? kWideTailRows : 0;
   a.head_blocks = (m.rows - a.tail_rows + RPW - 1) / RPW;
   const dim3 grid((unsigned)(a.head_blocks + a.tail_rows));
   hipLaunchKernelGGL((k_mxnorm_wide<ELEM, GAMMA, HAD, W, STEPS, SRC>), grid, dim3(NW * kWave),

@@ -182,13 +182,17 @@ def test_mxnorm_edge_rows(elem, p, hidden):
         _check_mxnorm(xb, None, p, c, elem, what="edge no gamma c=%g" % c)
 
 
-@pytest.mark.parametrize("rows", [8191, 8192, 8193, 10001])
-@pytest.mark.parametrize("hidden", [3072, 4064, 4096])
+@pytest.mark.parametrize("rows,hidden", [(r, h) for r in (8191, 8192, 8193, 10001)
+                                         for h in (3072, 4064, 4096)] +
+                         [(r, h) for r in (8192, 8193) for h in (4608, 5152, 6144, 8192)])
 def test_mxnorm_wide_tail_part(rows, hidden):
-    """E4M3 launches of 8192 rows or more over 2048 < hidden <= 4096 hand
-    their last 2048 rows to workgroups of one row and 4 waves: the boundary
-    between the two parts (odd row counts leave the last 2-row workgroup half
-    empty), ragged widths, and edge rows placed in the tail part."""
+    """E4M3 launches of 8192 rows or more with rows of 2 waves of 4 to 8
+    steps (3072 < hidden <= 8192) hand their last 2048 rows to workgroups of
+    one row and 4 waves of half as many steps (3072: 3 steps, no tail part):
+    the boundary between the two parts (odd row counts leave the last 2-row
+    workgroup half empty), ragged widths (4064; 4608 and 5152: 5 and 6 steps
+    with a ragged last one, the tail part's last step past the row end), and
+    edge rows placed in the tail part."""
     xb, gb = W.generate(rows, hidden, "rowscale", seed=rows + hidden)
     e = _edge_rows(hidden)
     xb[rows - 1 - len(e):rows - 1] = e          # in the tail part
