@@ -380,16 +380,17 @@ __global__ __launch_bounds__(W * 64) void k_mxnorm_bwd_wide(const BwdArgs a) {
   }
   if constexpr (GAMMA) {
     // this wave's columns of the workgroup's partial row; rows of 8 waves of
-    // 1 or 2 steps store them non-temporally (measured on MI355X: 16384 x
-    // 4096 66.8 against 67.4 us, 8192 x 8192 68.3 against 68.9, 32768 x 4096
-    // 127.5 against 128.5; with 3 waves, 8 steps or one wave per row it was
-    // 0.5-2% slower)
+    // 1 or 2 steps and rows of 4 waves store them non-temporally (measured on
+    // MI355X: 16384 x 4096 66.8 against 67.4 us, 8192 x 8192 68.3 against
+    // 68.9, 32768 x 4096 127.5 against 128.5, 4096 x 16384 77.3 against 78.0,
+    // 4096 x 10240 49.3 against 49.6; with 3 waves, 8 waves of 5 to 8 steps or
+    // one wave per row it was 0.5-2% slower)
     float* prow = a.partial + (int64_t)blockIdx.x * a.hidden;
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       if (!act[s]) continue;
       float* dst = prow + (choff[s] >> 4) * 8;
-      if constexpr (W == 8 && STEPS <= 2) {
+      if constexpr ((W == 8 && STEPS <= 2) || W == 4) {
         store_nt_f4(dst, acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
         store_nt_f4(dst + 4, acc[s][4], acc[s][5], acc[s][6], acc[s][7]);
       } else {
